@@ -1,0 +1,234 @@
+"""Float64 / integer oracle of one rank's share of sequence-parallel DiT attention.
+
+TEST INFRASTRUCTURE ONLY (see oracle/__init__.py): used by tests, the smoke
+check and the benchmark's CPU-baseline leg, never by the product path.
+
+Sources (page title, then section):
+  [MH3] "HCCL AllGatherV 实战解析：MiniMax-H3-Comfy-NPU 中 DiT 序列并行与
+        peer-copy 双后端机制" (m.nxbn.cn/news/97331)
+        - section "机制一 DiT 序列并行": rank r owns the token range
+          [seq_len*r // world_size, seq_len*(r+1) // world_size) of the packed
+          sequence h; the RoPE frequency table is sliced with it; attention
+          takes Q from the local shard and K/V over the full sequence; after the
+          last block the per-rank outputs are joined back along the sequence.
+        - section "机制二 ... 后端 A: HCCL AllGatherV": every rank contributes
+          `counts` elements placed at `displacements` (element offsets) of a
+          one-dimensional receive buffer; each rank's block is then narrowed,
+          viewed back to that rank's shape and concatenated.
+  [HY3] "NPU HunyuanImage-3.0模型推理优化实践" (cf-1.com/news/2296994)
+        - section "消除旋转位置编码冗余cast算子": rotary embedding is applied to
+          the query and key states only, with cos/sin tables
+          (apply_rotary_pos_emb(query_states, key_states, cos, sin)).
+        - section "消除FA中scale的冗余计算": the attention scale is 1/sqrt(d),
+          computed once.
+
+Readings where the pages are silent are listed in the design notes of the
+repository; the ones that shape the arithmetic here are: integer division is
+floor on non-negative Python ints; RoPE is the usual rotary form with
+frequencies theta**(-2j/d) at the token's absolute packed index, pairing
+(j, j + d/2) ("half" style, the rotate_half convention) or (2j, 2j+1)
+("interleaved"); attention is unmasked (bidirectional) softmax attention.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# Shard arithmetic  [MH3, 机制一]
+# ---------------------------------------------------------------------------
+
+
+def shard_bounds(S: int, W: int, r: int) -> tuple[int, int]:
+    """Token range [a, b) of rank r when S packed tokens are split over W ranks.
+
+    [MH3, 机制一]: a = S*r // W, b = S*(r+1) // W (the '+' of r+1 is lost in
+    the page text).  Exact Python integers, no overflow.
+    """
+    S, W, r = int(S), int(W), int(r)
+    if W < 1 or not (0 <= r < W) or S < 0:
+        raise ValueError("need W >= 1, 0 <= r < W, S >= 0")
+    return (S * r) // W, (S * (r + 1)) // W
+
+
+def all_shard_bounds(S: int, W: int) -> list[tuple[int, int]]:
+    """[shard_bounds(S, W, r) for every rank r]."""
+    return [shard_bounds(S, W, r) for r in range(W)]
+
+
+def allgatherv_layout(S: int, W: int, outer: int = 1, inner: int = 1):
+    """AllGatherV counts and displacements, in elements  [MH3, 后端 A].
+
+    Rank r sends its local tensor of shape [outer, s_r, inner] flattened, so
+    counts[r] = outer * s_r * inner; the receive buffer holds the ranks' blocks
+    back to back in rank order, so displs[r] = counts[0] + ... + counts[r-1].
+    """
+    counts = []
+    for r in range(W):
+        a, b = shard_bounds(S, W, r)
+        counts.append(int(outer) * (b - a) * int(inner))
+    displs = []
+    off = 0
+    for c in counts:
+        displs.append(off)
+        off += c
+    return counts, displs
+
+
+# ---------------------------------------------------------------------------
+# AllGatherV data movement  [MH3, 后端 A]
+# ---------------------------------------------------------------------------
+
+
+def varlen_pack(sends, counts, displs, flat: np.ndarray) -> np.ndarray:
+    """Gather step of AllGatherV: flat[displs[r] + i] = sends[r].ravel()[i].
+
+    Returns a copy of `flat` with every rank's block written; elements that no
+    block covers keep their previous value.  Bits are copied unchanged.
+    """
+    out = np.array(flat, copy=True)
+    for r, src in enumerate(sends):
+        c, dsp = int(counts[r]), int(displs[r])
+        src = np.asarray(src).reshape(-1)
+        if src.size < c:
+            raise ValueError("send buffer shorter than its count")
+        if dsp < 0 or dsp + c > out.size:
+            raise ValueError("block outside the receive buffer")
+        out[dsp:dsp + c] = src[:c]
+    return out
+
+
+def varlen_unpack(flat: np.ndarray, displs, seq_lens, outer: int, inner: int) -> np.ndarray:
+    """narrow -> view -> concat of an AllGatherV receive buffer  [MH3, 后端 A].
+
+    Rank r's block flat[displs[r] : displs[r] + outer*s_r*inner] is viewed as
+    [outer, s_r, inner]; the views are concatenated along the sequence axis,
+    giving [outer, sum(s_r), inner].
+    """
+    parts = []
+    for r, s in enumerate(seq_lens):
+        n = int(outer) * int(s) * int(inner)
+        dsp = int(displs[r])
+        parts.append(np.asarray(flat)[dsp:dsp + n].reshape(int(outer), int(s), int(inner)))
+    return np.concatenate(parts, axis=1)
+
+
+def output_concat(outs) -> np.ndarray:
+    """Final merge of the per-rank outputs along the sequence  [MH3, 机制一]."""
+    return np.concatenate([np.asarray(o) for o in outs], axis=0)
+
+
+# ---------------------------------------------------------------------------
+# Rotary position embedding on the local slice  [MH3, 机制一; HY3]
+# ---------------------------------------------------------------------------
+
+
+def rope_inv_freq(d: int, theta: float = 10000.0) -> np.ndarray:
+    """Frequencies theta**(-2j/d), j = 0 .. d/2-1, in float64."""
+    j = np.arange(d // 2, dtype=np.float64)
+    return np.power(np.float64(theta), -2.0 * j / np.float64(d))
+
+
+def rope_apply(x: np.ndarray, pos0: int, theta: float = 10000.0, style: str = "half") -> np.ndarray:
+    """Rotate each pair of x [s, H, d] by angle p * theta**(-2j/d), p = pos0 + token.
+
+    The rank's slice of the frequency table starts at its first absolute
+    position pos0 [MH3, 机制一].  For pair j with components (x1, x2) the result
+    is (x1 cos - x2 sin, x2 cos + x1 sin) (rotate_half form [HY3]).  Pairs are
+    (j, j + d/2) for style "half" and (2j, 2j+1) for "interleaved".
+    Float64 throughout.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    s, H, d = x.shape
+    if d % 2:
+        raise ValueError("d must be even")
+    pos = np.float64(pos0) + np.arange(s, dtype=np.float64)
+    ang = pos[:, None] * rope_inv_freq(d, theta)[None, :]          # [s, d/2]
+    cos = np.cos(ang)[:, None, :]                                   # [s, 1, d/2]
+    sin = np.sin(ang)[:, None, :]
+    if style == "half":
+        x1, x2 = x[..., : d // 2], x[..., d // 2:]
+    elif style == "interleaved":
+        x1, x2 = x[..., 0::2], x[..., 1::2]
+    else:
+        raise ValueError("style must be 'half' or 'interleaved'")
+    y1 = x1 * cos - x2 * sin
+    y2 = x2 * cos + x1 * sin
+    y = np.empty_like(x)
+    if style == "half":
+        y[..., : d // 2], y[..., d // 2:] = y1, y2
+    else:
+        y[..., 0::2], y[..., 1::2] = y1, y2
+    return y
+
+
+# ---------------------------------------------------------------------------
+# Attention of local queries against the full sequence  [MH3, 机制一; HY3]
+# ---------------------------------------------------------------------------
+
+
+def _attend_head(qh: np.ndarray, kh: np.ndarray, vh: np.ndarray, scale: float, row_block: int):
+    """softmax(scale * qh kh^T) vh and the natural-log LSE for one head, float64.
+
+    Query rows are independent, so they are taken row_block at a time only to
+    bound memory; every row is the plain definition.
+    """
+    sq = qh.shape[0]
+    o = np.empty((sq, vh.shape[1]), dtype=np.float64)
+    lse = np.empty(sq, dtype=np.float64)
+    for i0 in range(0, sq, row_block):
+        i1 = min(sq, i0 + row_block)
+        logits = (qh[i0:i1] @ kh.T) * np.float64(scale)            # [rows, skv]
+        m = logits.max(axis=1, keepdims=True)
+        e = np.exp(logits - m)
+        z = e.sum(axis=1, keepdims=True)
+        o[i0:i1] = (e / z) @ vh
+        lse[i0:i1] = (m + np.log(z))[:, 0]
+    return o, lse
+
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float | None = None,
+              row_block: int = 1024):
+    """O[i,h,:] = sum_j softmax_j(scale <q_ih, k_jh>) v_jh, unmasked  [MH3, 机制一].
+
+    q [sq, H, d] are the rank's local (rotated) queries, k and v [skv, H, d] the
+    full gathered sequence.  scale defaults to 1/sqrt(d) [HY3].  Returns
+    (O [sq, H, d], LSE [H, sq]) in float64, LSE = log sum_j exp(scale <q, k_j>).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    sq, H, d = q.shape
+    if k.shape[1:] != (H, d) or v.shape != k.shape:
+        raise ValueError("shape mismatch")
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    o = np.empty((sq, H, d), dtype=np.float64)
+    lse = np.empty((H, sq), dtype=np.float64)
+    for h in range(H):
+        o[:, h, :], lse[h] = _attend_head(q[:, h, :], k[:, h, :], v[:, h, :], scale, row_block)
+    return o, lse
+
+
+def attention_rows(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float | None = None,
+                   widen=None):
+    """attention() for a few query rows against a (possibly huge) K/V.
+
+    Identical definition; K and V are widened to float64 one head at a time so
+    that full-size sequences fit in host memory.  `widen` maps a raw [skv, d]
+    head slice to float64 (default: np.asarray(..., float64)); callers holding
+    bf16 bit patterns pass a widening function from the input generator.
+    """
+    if widen is None:
+        def widen(a):
+            return np.asarray(a, dtype=np.float64)
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    n, H, d = q_rows.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    o = np.empty((n, H, d), dtype=np.float64)
+    lse = np.empty((H, n), dtype=np.float64)
+    for h in range(H):
+        kh = widen(k[:, h, :])
+        vh = widen(v[:, h, :])
+        o[:, h, :], lse[h] = _attend_head(q_rows[:, h, :], kh, vh, scale, row_block=256)
+    return o, lse
