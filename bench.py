@@ -1,0 +1,199 @@
+#!/usr/bin/env python3
+"""Benchmark of one rank's share of packed-token sequence-parallel DiT attention.
+
+One step = the whole hot path of one rank on one MI355X: RoPE of the local Q
+and K slice, AllGatherV of K and V (pack into the flat buffer + unpack), the
+attention of the local Q shard against the full K/V, and the AllGatherV of
+the per-rank outputs.  Default workload: the 768P/15 s-like sequence
+(S = 367,287 packed tokens, W = 4 simulated ranks, rank 0 holds 91,821 query
+tokens, 24 heads x 128, bf16).  Inputs are resident in HBM before timing.
+
+Prints ONE JSON line.  `value` = attention FLOP of a step / wall time of the
+whole step (TFLOP/s); per-kernel times come from HIP events recorded on the
+stream the kernels run on (torch's current stream) over the timed region.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "shard-attention TFLOP/s (% bf16 MFMA peak) + varlen pack GB/s (% HBM), 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+ATTN_SRC = os.path.join(ROOT, "sequence_dit_attention_amd", "csrc", "attn_bf16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_traffic.json")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    with open(ATTN_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profiles(wl_name: str):
+    """HBM bytes per attention launch from the committed rocprofv3 PMC summary,
+    or None when it is missing or the kernel source changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sha256_16") != kernel_hash() or t.get("workload") != wl_name:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, q, k, v, a, b, rows: int):
+    """The fp64 oracle on a bounded sample: `rows` query rows of the rank's shard
+    (all heads) against the full K/V.  Only the oracle's attention is timed;
+    widening the bf16 head slices to fp64 is set-up.  Returns the cpu_baseline object."""
+    import numpy as np
+
+    import oracle
+    from synth import bf16_bits_to_f32
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    idx = np.linspace(a, b - 1, rows).astype(np.int64)
+    qrows = bf16_bits_to_f32(q[idx]).astype(np.float64)
+    spent = 0.0
+    for h in range(wl.H):
+        kh = bf16_bits_to_f32(k[:, h:h + 1, :]).astype(np.float64)
+        vh = bf16_bits_to_f32(v[:, h:h + 1, :]).astype(np.float64)
+        t0 = time.perf_counter()
+        oracle.attention(qrows[:, h:h + 1, :], kh, vh)
+        spent += time.perf_counter() - t0
+    flops = 4.0 * rows * wl.S * wl.H * wl.d
+    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{rows} query rows x {wl.H} heads of the rank-{wl.ranks[0]} shard against the full "
+                      f"{wl.S}-token K/V (fp64 numpy oracle attention, {spent:.1f} s)"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="p768_15s_w4")
+    ap.add_argument("--cpu-rows", type=int, default=48, help="query rows in the CPU-oracle sample (0: skip)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (--gpus {args.gpus} "
+              "requested). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from sequence_dit_attention_amd.pipeline import RankShare
+    from synth import gen_qkv, get_workload
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    wl = get_workload(args.workload)
+    if wl.dtype != "bf16":
+        print("bench.py times the bf16 workloads", file=sys.stderr)
+        return 1
+    r = wl.ranks[0]
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    log(f"workload {wl.name}: S={wl.S} W={wl.W} rank={r} H={wl.H} d={wl.d}; generating inputs")
+    q, k, v = gen_qkv(wl)
+
+    def up(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    share = RankShare(wl.S, wl.W, r, wl.H, wl.d, torch.bfloat16, wl.theta, dev)
+    share.set_inputs(up(q), up(k), up(v))
+    torch.cuda.synchronize()
+    log(f"inputs resident after {time.time() - t0:.1f}s; warmup {args.warmup} steps")
+
+    for _ in range(args.warmup):
+        share.step()
+    torch.cuda.synchronize()
+
+    stages = ["rope", "pack_kv", "unpack_kv", "attn", "concat_out"]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        e = ev[i]
+        e[0].record()
+        share.rope()
+        e[1].record()
+        share.gather_kv_pack()
+        e[2].record()
+        share.gather_kv_unpack()
+        e[3].record()
+        share.attend()
+        e[4].record()
+        share.concat_out()
+        e[5].record()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms_step = start.elapsed_time(stop) / args.steps
+    per = {s: sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)) / args.steps
+           for j, s in enumerate(stages)}
+    log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (host wall {wall / args.steps * 1e3:.3f} ms); "
+        + ", ".join(f"{s} {t:.3f} ms" for s, t in per.items()))
+
+    flops = share.attn_flops()
+    attn_tflops = flops / (per["attn"] * 1e-3) / 1e12
+    pack_bytes = share.pack_kv_bytes()
+    pack_gbs = pack_bytes / (per["pack_kv"] * 1e-3) / 1e9
+    unpack_gbs = pack_bytes / (per["unpack_kv"] * 1e-3) / 1e9
+    traffic = traffic_from_profiles(wl.name)
+    out = {
+        "metric": METRIC,
+        "value": flops / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "S": wl.S, "W": wl.W, "rank": r, "sq": share.b - share.a,
+                   "H": wl.H, "d": wl.d, "theta": wl.theta},
+        "roofline": {"bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": attn_tflops / PEAK_BF16_TFLOPS, "traffic": traffic},
+        "kernels": {
+            "attn_ms": per["attn"], "attn_tflops": attn_tflops, "attn_frac_mfma_peak": attn_tflops / PEAK_BF16_TFLOPS,
+            "pack_kv_ms": per["pack_kv"], "pack_kv_gbs": pack_gbs, "pack_frac_hbm_peak": pack_gbs / PEAK_HBM_GBS,
+            "unpack_kv_ms": per["unpack_kv"], "unpack_kv_gbs": unpack_gbs,
+            "rope_ms": per["rope"], "concat_out_ms": per["concat_out"],
+            "attn_kernel_sha256_16": kernel_hash(),
+        },
+    }
+    if args.cpu_rows > 0:
+        log(f"CPU oracle baseline on {args.cpu_rows} rows")
+        out["cpu_baseline"] = cpu_baseline(wl, q, k, v, share.a, share.b, args.cpu_rows)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

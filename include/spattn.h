@@ -1,0 +1,178 @@
+/*
+ * spattn.h -- C ABI of libspattn.so: one rank's share of packed-token
+ * sequence-parallel DiT self-attention on AMD Instinct MI355X (gfx950).
+ *
+ * The method (page "HCCL AllGatherV 实战解析：MiniMax-H3-Comfy-NPU 中 DiT 序列并行与
+ * peer-copy 双后端机制", sections 机制一 and 机制二/后端 A): a packed audio+video
+ * token sequence of S tokens is split over W ranks; each rank rotates its
+ * local slice with RoPE, the ranks' K/V shards are reassembled into the full
+ * sequence with AllGatherV semantics (per-rank element counts and
+ * displacements into one flat buffer, then narrow/view/concat), attention runs
+ * with the rank's local queries against the full K/V, and the per-rank outputs
+ * are concatenated back along the sequence.
+ *
+ * Conventions shared by every entry point
+ *  - Tensors are dense, contiguous and token-major: [tokens, H, d] (batch 1).
+ *  - Element types: SP_F32 (IEEE binary32) or SP_BF16 (bfloat16 bit patterns).
+ *  - Counts, displacements and lengths are in ELEMENTS, as in AllGatherV.
+ *  - Device pointers are HIP device memory of the current device; host arrays
+ *    are read during the call only.  The caller allocates and frees every
+ *    buffer; the library keeps no pointer after a call returns and makes no
+ *    device allocation.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
+ *    is enqueued asynchronously on it; nothing synchronises with the host.
+ *    The caller synchronises the stream before reading results, as the
+ *    page's collective path does (async on the current stream, then one
+ *    synchronize()).  Faults during execution therefore surface at the
+ *    caller's synchronisation.
+ *  - Every argument is validated on the host before anything is enqueued; on
+ *    error nothing is enqueued, a negative status is returned and
+ *    sp_last_error() describes the failure.  There is no fallback path.
+ */
+#ifndef SPATTN_H
+#define SPATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPATTN_ABI_VERSION 1
+
+/* Status codes. */
+enum {
+  SP_OK = 0,
+  SP_EINVAL = -1,        /* malformed argument (negative size, null pointer with data, bad enum) */
+  SP_EUNSUPPORTED = -2,  /* well-formed but not implemented (head size, dtype) */
+  SP_ERANGE = -3,        /* a block or index falls outside its buffer, or a size overflows int64 */
+  SP_EOVERLAP = -4,      /* destination blocks overlap each other, or an output overlaps an input */
+  SP_EHIP = -5           /* the HIP runtime refused a launch; message holds the HIP error */
+};
+
+/* Element types. */
+enum { SP_F32 = 0, SP_BF16 = 1 };
+
+/* RoPE pairings: (j, j + d/2) ("rotate_half") or (2j, 2j + 1). */
+enum { SP_ROPE_HALF = 0, SP_ROPE_INTERLEAVED = 1 };
+
+/* ABI version of the loaded library (SPATTN_ABI_VERSION). */
+int sp_abi_version(void);
+
+/* Message of the last failing call on this thread ("" if none).  The string
+ * is owned by the library and valid until the next call on the same thread. */
+const char* sp_last_error(void);
+
+/*
+ * sp_shard_bounds -- token range [*start, *end) of rank r.
+ * Defined by section 机制一: rank r owns [S*r // W, S*(r+1) // W) (floor
+ * division; computed exactly in 128-bit integers, so any S >= 0 is valid).
+ * Shards differ in length by at most one token when W does not divide S; a
+ * rank may own zero tokens when S < W.
+ * Errors: SP_EINVAL if W < 1, r outside [0, W), S < 0 or a null output.
+ * Host-only: touches no device.
+ */
+int sp_shard_bounds(int64_t S, int32_t W, int32_t r, int64_t* start, int64_t* end);
+
+/*
+ * sp_allgatherv_layout -- AllGatherV counts and displacements (elements).
+ * Defined by section 后端 A (counts = element counts per rank,
+ * displacements = target offsets in the flat receive buffer).  Rank r's
+ * local tensor has shape [outer, s_r, inner]; counts[r] = outer*s_r*inner and
+ * displs[r] = counts[0] + ... + counts[r-1] (rank order, no gaps).
+ * counts and displs are host arrays of W entries written by the call.
+ * Errors: SP_EINVAL (W < 1, negative outer/inner, null arrays),
+ * SP_ERANGE (outer*S*inner overflows int64).  Host-only.
+ */
+int sp_allgatherv_layout(int64_t S, int32_t W, int64_t outer, int64_t inner,
+                         int64_t* counts, int64_t* displs);
+
+/*
+ * varlen_pack -- the data movement of one AllGatherV into a flat buffer.
+ * Defined by section 后端 A: for every rank r and 0 <= i < counts[r],
+ * flat[displs[r] + i] = send[r][i].  Bits are copied unchanged; elements of
+ * `flat` outside every block are left untouched.
+ *   send    host array of W device pointers (rank r's shard, counts[r] elements)
+ *   counts  host array of W element counts (>= 0)
+ *   displs  host array of W element offsets into flat (>= 0), any order,
+ *           gaps allowed (MPI AllGatherV semantics)
+ *   flat    device buffer of flat_elems elements
+ * Errors: SP_EINVAL (bad dtype, W < 1, negative count/displacement, null
+ * pointer with a nonzero count), SP_ERANGE (a block past flat_elems),
+ * SP_EOVERLAP (two blocks overlap, or a source overlaps flat), SP_EHIP.
+ */
+int varlen_pack(int32_t dtype, int32_t W, const void* const* send,
+                const int64_t* counts, const int64_t* displs,
+                void* flat, int64_t flat_elems, void* stream);
+
+/*
+ * varlen_unpack -- narrow -> view -> concat of an AllGatherV receive buffer.
+ * Defined by section 后端 A: rank r's block of flat, starting at displs[r] and
+ * holding outer*seq_lens[r]*inner elements, is viewed as
+ * [outer, seq_lens[r], inner]; the views are concatenated along the sequence
+ * axis into out = [outer, sum(seq_lens), inner]:
+ *   out[o, a_r + t, k] = flat[displs[r] + (o*seq_lens[r] + t)*inner + k],
+ *   a_r = seq_lens[0] + ... + seq_lens[r-1].
+ * With outer == 1 every rank's block is one contiguous copy.
+ *   flat      device buffer of flat_elems elements (read)
+ *   displs, seq_lens  host arrays of W entries
+ *   out       device buffer of outer*sum(seq_lens)*inner elements (written)
+ * Errors: SP_EINVAL (bad dtype, W < 1, negative sizes, null pointers with
+ * data), SP_ERANGE (a block past flat_elems, size overflow), SP_EOVERLAP
+ * (blocks overlap each other, or out overlaps flat), SP_EHIP.
+ */
+int varlen_unpack(int32_t dtype, int32_t W, const void* flat, int64_t flat_elems,
+                  const int64_t* displs, const int64_t* seq_lens,
+                  int64_t outer, int64_t inner, void* out, void* stream);
+
+/*
+ * rope_apply -- rotary position embedding of a rank's local slice.
+ * Section 机制一 slices the RoPE frequency table with the rank's token range,
+ * so positions are absolute: token t of the slice sits at p = pos0 + t (pos0
+ * is the rank's start from sp_shard_bounds).  Page "NPU HunyuanImage-3.0模型推理
+ * 优化实践", section 消除旋转位置编码冗余cast算子, applies the rotation to query
+ * and key states only (apply_rotary_pos_emb(q, k, cos, sin)); V is never
+ * rotated.  For pair j in 0 .. d/2-1 with angle phi = p * theta^(-2j/d):
+ *   y1 = x1 cos(phi) - x2 sin(phi),  y2 = x2 cos(phi) + x1 sin(phi),
+ * pairs (x1, x2) = (x[j], x[j + d/2]) for SP_ROPE_HALF and (x[2j], x[2j+1])
+ * for SP_ROPE_INTERLEAVED.  phi and its range reduction are float64, the
+ * rotation float32, the result rounded to dtype (nearest-even).
+ *   x, y  device [s, H, d] of dtype; y == x (in place) is allowed, any other
+ *         overlap is not.
+ * Errors: SP_EINVAL (bad dtype/style, s < 0, H < 1, d odd or > 1024,
+ * theta not finite and > 0, |pos0| or |pos0 + s| >= 2^53, null pointers
+ * with data), SP_EOVERLAP (partial overlap of x and y), SP_EHIP.
+ */
+int rope_apply(int32_t dtype, const void* x, void* y, int64_t s, int32_t H, int32_t d,
+               int64_t pos0, double theta, int32_t style, void* stream);
+
+/*
+ * shard_attn_fwd -- attention of the rank's local queries against the full
+ * gathered sequence.  Section 机制一: Q comes from the local shard while K/V
+ * must cover the whole sequence.  Unmasked (bidirectional) softmax attention:
+ *   O[i,h,:] = sum_j softmax_j(scale * <q[i,h,:], k[j,h,:]>) v[j,h,:]
+ * for 0 <= i < sq, 0 <= j < skv.  The scale is computed once by the caller
+ * (1/sqrt(d) in page "NPU HunyuanImage-3.0模型推理优化实践", section
+ * 消除FA中scale的冗余计算) and passed in.
+ *   q    device [sq, H, d];  k, v  device [skv, H, d];  o  device [sq, H, d]
+ *   lse  NULL or device float32 [H, sq]: natural-log log-sum-exp of the
+ *        scaled logits of each (head, query) row.
+ * SP_BF16: bf16 operands, float32 accumulation and float32 online softmax,
+ * probabilities rounded to bf16 for the P*V product, O rounded to bf16.
+ * SP_F32: float32 throughout.  Each output row depends only on its own query
+ * row and on K/V, in a fixed key order, so results are deterministic and a
+ * row's result does not depend on sq or on where the row sits in q.
+ * Errors: SP_EINVAL (bad dtype, sq < 0, skv < 1, H < 1, scale not finite or
+ * <= 0, null pointers with data), SP_EUNSUPPORTED (d not 64 or 128),
+ * SP_ERANGE (sizes beyond the kernel's 32-bit grid), SP_EOVERLAP (o or lse
+ * overlaps an input or each other), SP_EHIP.  sq == 0 enqueues nothing.
+ */
+int shard_attn_fwd(int32_t dtype, const void* q, const void* k, const void* v,
+                   void* o, float* lse, int64_t sq, int64_t skv, int32_t H, int32_t d,
+                   float scale, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPATTN_H */

@@ -1,0 +1,18 @@
+"""MI355X-native (gfx950) one-rank share of packed-token sequence-parallel DiT attention.
+
+The computation lives in libspattn.so (C ABI declared in include/spattn.h);
+this package only loads it and marshals torch tensors into its calls.
+"""
+from .api import (  # noqa: F401
+    SP_BF16,
+    SP_F32,
+    exchange_sim,
+    rope_apply,
+    shard_attn_fwd,
+    sp_abi_version,
+    sp_allgatherv_layout,
+    sp_shard_bounds,
+    varlen_pack,
+    varlen_unpack,
+)
+from ._lib import LIB_PATH, SpattnError, lib  # noqa: F401

@@ -1,0 +1,154 @@
+"""Torch-facing wrappers of the libspattn C ABI (argument marshalling only).
+
+Each function has the name of the C entry point it calls.  Device tensors
+must be contiguous HIP tensors of the right dtype; work is enqueued on
+torch's current stream and nothing is synchronised.  Every computation runs
+in the HIP library: there is no CPU or PyTorch fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+
+import torch
+
+from ._lib import check, lib
+
+SP_F32, SP_BF16 = 0, 1
+SP_ROPE_HALF, SP_ROPE_INTERLEAVED = 0, 1
+_STYLES = {"half": SP_ROPE_HALF, "interleaved": SP_ROPE_INTERLEAVED}
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SP_F32
+    if t.dtype == torch.bfloat16:
+        return SP_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _i64s(vals):
+    arr = (ctypes.c_int64 * len(vals))(*[int(x) for x in vals])
+    return arr
+
+
+def sp_abi_version() -> int:
+    return int(lib().sp_abi_version())
+
+
+def sp_shard_bounds(S: int, W: int, r: int) -> tuple[int, int]:
+    a, b = ctypes.c_int64(), ctypes.c_int64()
+    check("sp_shard_bounds", lib().sp_shard_bounds(S, W, r, ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
+
+
+def sp_allgatherv_layout(S: int, W: int, outer: int = 1, inner: int = 1):
+    counts, displs = (ctypes.c_int64 * max(W, 1))(), (ctypes.c_int64 * max(W, 1))()
+    check("sp_allgatherv_layout", lib().sp_allgatherv_layout(S, W, outer, inner, counts, displs))
+    return list(counts)[:W], list(displs)[:W]
+
+
+def varlen_pack(sends, counts, displs, flat: torch.Tensor) -> torch.Tensor:
+    """flat[displs[r] : displs[r] + counts[r]] = sends[r] (flattened), in place on `flat`."""
+    code = _dtype_code(flat)
+    W = len(sends)
+    ptrs = (ctypes.c_void_p * W)()
+    for r, s in enumerate(sends):
+        if s.dtype != flat.dtype:
+            raise TypeError("send and flat dtypes differ")
+        if int(counts[r]) > s.numel():
+            raise ValueError(f"send[{r}] holds fewer than counts[{r}] elements")
+        ptrs[r] = _dev(s, f"send[{r}]") if s.numel() else None
+    check("varlen_pack", lib().varlen_pack(code, W, ptrs, _i64s(counts), _i64s(displs),
+                                           _dev(flat, "flat"), flat.numel(), _stream(flat)))
+    return flat
+
+
+def varlen_unpack(flat: torch.Tensor, displs, seq_lens, outer: int, inner: int,
+                  out: torch.Tensor) -> torch.Tensor:
+    """out[o, a_r + t, k] = flat[displs[r] + (o*seq_lens[r] + t)*inner + k], in place on `out`."""
+    code = _dtype_code(flat)
+    if out.dtype != flat.dtype:
+        raise TypeError("flat and out dtypes differ")
+    need = int(outer) * sum(int(s) for s in seq_lens) * int(inner)
+    if out.numel() != need:
+        raise ValueError(f"out must hold outer*sum(seq_lens)*inner = {need} elements")
+    W = len(seq_lens)
+    check("varlen_unpack", lib().varlen_unpack(code, W, _dev(flat, "flat"), flat.numel(), _i64s(displs),
+                                               _i64s(seq_lens), outer, inner, _dev(out, "out"),
+                                               _stream(flat)))
+    return out
+
+
+def rope_apply(x: torch.Tensor, pos0: int, theta: float = 10000.0, style: str = "half",
+               out: torch.Tensor | None = None) -> torch.Tensor:
+    """RoPE of x [s, H, d] at positions pos0 + t; in place when out is None or out is x."""
+    if x.dim() != 3:
+        raise ValueError("x must be [s, H, d]")
+    y = x if out is None else out
+    if y.shape != x.shape or y.dtype != x.dtype:
+        raise ValueError("out must match x in shape and dtype")
+    s, H, d = x.shape
+    check("rope_apply", lib().rope_apply(_dtype_code(x), _dev(x, "x"), _dev(y, "out"), s, H, d, int(pos0),
+                                         float(theta), _STYLES[style], _stream(x)))
+    return y
+
+
+def shard_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor | None = None,
+                   lse: torch.Tensor | None = None, scale: float | None = None) -> torch.Tensor:
+    """Attention of q [sq, H, d] against k, v [skv, H, d]; returns O [sq, H, d] (lse [H, sq] if given)."""
+    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape or q.shape[1:] != k.shape[1:]:
+        raise ValueError("q [sq,H,d], k and v [skv,H,d] with matching H, d")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v dtypes differ")
+    sq, H, d = q.shape
+    skv = k.shape[0]
+    if out is None:
+        out = torch.empty_like(q)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    lp = None
+    if lse is not None:
+        if lse.dtype != torch.float32 or lse.shape != (H, sq):
+            raise ValueError("lse must be float32 [H, sq]")
+        lp = _dev(lse, "lse")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    check("shard_attn_fwd", lib().shard_attn_fwd(_dtype_code(q), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"),
+                                                 _dev(out, "out"), lp, sq, skv, H, d, float(scale),
+                                                 _stream(q)))
+    return out
+
+
+def exchange_sim(shards, cat_dim: int = 0):
+    """Single-GPU stand-in for exchange(rank, tensors, cat_dims): AllGatherV of
+    per-rank shards (list of tensors equal except along cat_dim) through a flat
+    buffer, then narrow/view/concat.  Returns the concatenated tensor."""
+    ref = shards[0]
+    shape = list(ref.shape)
+    outer = math.prod(shape[:cat_dim])
+    inner = math.prod(shape[cat_dim + 1:])
+    lens = [int(s.shape[cat_dim]) for s in shards]
+    counts = [outer * n * inner for n in lens]
+    displs, off = [], 0
+    for c in counts:
+        displs.append(off)
+        off += c
+    flat = torch.empty(off, dtype=ref.dtype, device=ref.device)
+    varlen_pack([s.reshape(-1) for s in shards], counts, displs, flat)
+    shape[cat_dim] = sum(lens)
+    out = torch.empty(shape, dtype=ref.dtype, device=ref.device)
+    varlen_unpack(flat, displs, lens, outer, inner, out)
+    return out

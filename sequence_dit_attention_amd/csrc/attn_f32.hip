@@ -1,0 +1,102 @@
+// Float32 attention of local queries against the full K/V (no mask).
+//
+// Page "HCCL AllGatherV 实战解析：MiniMax-H3-Comfy-NPU ...", section 机制一: Q
+// from the rank's shard, K/V over the whole sequence.  This is the small,
+// float32 path: one lane per (query row, head), K/V tiles of 32 keys staged in
+// LDS and read as broadcasts, and the usual online softmax (running max,
+// rescaled running sum and accumulator) in float32, base 2 with the scale
+// folded into log2(e).
+#include "internal.h"
+
+namespace spattn {
+namespace {
+
+constexpr int kRows = 64;  // query rows (lanes) per work-group: one wave
+constexpr int kBN = 32;    // keys per LDS tile
+
+template <int D>
+__global__ __launch_bounds__(kRows) void attn_f32_kernel(const float* __restrict__ q,
+                                                         const float* __restrict__ k,
+                                                         const float* __restrict__ v, float* __restrict__ o,
+                                                         float* __restrict__ lse, int64_t sq, int64_t skv,
+                                                         int H, float c /* scale * log2(e) */,
+                                                         int64_t nqt) {
+  __shared__ float ks[kBN][D];
+  __shared__ float vs[kBN][D];
+  const int64_t wg = blockIdx.x;
+  const int h = int(wg / nqt);
+  const int64_t i = (wg % nqt) * kRows + threadIdx.x;
+  const bool live = i < sq;
+
+  float qr[D], acc[D];
+  const float* qp = q + (i * H + h) * D;
+#pragma unroll
+  for (int e = 0; e < D; ++e) {
+    qr[e] = live ? qp[e] : 0.f;
+    acc[e] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+
+  for (int64_t j0 = 0; j0 < skv; j0 += kBN) {
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < kBN * D; idx += kRows) {
+      const int r = idx / D, e = idx % D;
+      const int64_t j = j0 + r;
+      ks[r][e] = j < skv ? k[(j * H + h) * D + e] : 0.f;
+      vs[r][e] = j < skv ? v[(j * H + h) * D + e] : 0.f;
+    }
+    __syncthreads();
+    float sc[kBN];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < kBN; ++r) {
+      float dot = 0.f;
+#pragma unroll
+      for (int e = 0; e < D; ++e) dot = fmaf(qr[e], ks[r][e], dot);
+      sc[r] = (j0 + r < skv) ? dot * c : -INFINITY;
+      mx = fmaxf(mx, sc[r]);
+    }
+    const float mn = fmaxf(m, mx);
+    const float alpha = exp2f(m - mn);
+    float rs = 0.f;
+#pragma unroll
+    for (int r = 0; r < kBN; ++r) {
+      sc[r] = exp2f(sc[r] - mn);
+      rs += sc[r];
+    }
+    l = l * alpha + rs;
+    m = mn;
+#pragma unroll
+    for (int e = 0; e < D; ++e) {
+      float a = acc[e] * alpha;
+#pragma unroll
+      for (int r = 0; r < kBN; ++r) a = fmaf(sc[r], vs[r][e], a);
+      acc[e] = a;
+    }
+  }
+  if (!live) return;
+  const float inv = 1.f / l;
+  float* op = o + (i * H + h) * D;
+#pragma unroll
+  for (int e = 0; e < D; ++e) op[e] = acc[e] * inv;
+  if (lse) lse[int64_t(h) * sq + i] = (m + log2f(l)) * 0.69314718055994531f;
+}
+
+}  // namespace
+
+hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                           int64_t sq, int64_t skv, int H, int d, float scale, hipStream_t stream) {
+  const int64_t nqt = (sq + kRows - 1) / kRows;
+  const int64_t grid = nqt * H;
+  if (grid > kMaxGrid) return hipErrorInvalidConfiguration;
+  const float c = scale * 1.4426950408889634f;
+  if (d == 64)
+    hipLaunchKernelGGL(attn_f32_kernel<64>, dim3(unsigned(grid)), dim3(kRows), 0, stream, q, k, v, o, lse,
+                       sq, skv, H, c, nqt);
+  else
+    hipLaunchKernelGGL(attn_f32_kernel<128>, dim3(unsigned(grid)), dim3(kRows), 0, stream, q, k, v, o,
+                       lse, sq, skv, H, c, nqt);
+  return hipGetLastError();
+}
+
+}  // namespace spattn

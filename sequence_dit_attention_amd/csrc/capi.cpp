@@ -1,0 +1,255 @@
+// Host side of libspattn.so: argument validation, error state and launches.
+// Every check runs before anything is enqueued; on failure nothing runs.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "../../include/spattn.h"
+#include "internal.h"
+
+using spattn::CopySeg;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return SP_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(SP_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
+bool add_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_add_overflow(a, b, out); }
+
+int elem_bytes(int32_t dtype) {
+  if (dtype == SP_F32) return 4;
+  if (dtype == SP_BF16) return 2;
+  return 0;
+}
+
+// Byte ranges [lo, hi) on the device address space.
+bool ranges_overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+  if (abytes <= 0 || bbytes <= 0) return false;
+  auto a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + static_cast<uintptr_t>(bbytes) && b0 < a0 + static_cast<uintptr_t>(abytes);
+}
+
+// Checks that the element blocks [displs[r], displs[r] + sizes[r]) with sizes > 0 are disjoint.
+bool blocks_disjoint(int32_t W, const int64_t* displs, const std::vector<int64_t>& sizes) {
+  std::vector<std::pair<int64_t, int64_t>> iv;
+  iv.reserve(W);
+  for (int32_t r = 0; r < W; ++r)
+    if (sizes[r] > 0) iv.emplace_back(displs[r], displs[r] + sizes[r]);
+  std::sort(iv.begin(), iv.end());
+  for (size_t i = 1; i < iv.size(); ++i)
+    if (iv[i].first < iv[i - 1].second) return false;
+  return true;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+int launch_copies(const std::vector<CopySeg>& segs, int64_t outer, void* stream) {
+  if (segs.empty() || outer == 0) return ok();
+  hipGetLastError();  // launches below report their own status
+  hipError_t e = spattn::launch_segcopy(segs.data(), static_cast<int>(segs.size()), outer,
+                                        as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "segmented copy launch");
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int sp_abi_version(void) { return SPATTN_ABI_VERSION; }
+
+const char* sp_last_error(void) { return g_err; }
+
+int sp_shard_bounds(int64_t S, int32_t W, int32_t r, int64_t* start, int64_t* end) {
+  if (!start || !end) return fail(SP_EINVAL, "sp_shard_bounds: null output pointer");
+  if (W < 1) return fail(SP_EINVAL, "sp_shard_bounds: W must be >= 1 (got %d)", W);
+  if (r < 0 || r >= W) return fail(SP_EINVAL, "sp_shard_bounds: rank %d outside [0, %d)", r, W);
+  if (S < 0) return fail(SP_EINVAL, "sp_shard_bounds: S must be >= 0 (got %lld)", (long long)S);
+  __int128 s = S;
+  *start = static_cast<int64_t>((s * r) / W);
+  *end = static_cast<int64_t>((s * (r + 1)) / W);
+  return ok();
+}
+
+int sp_allgatherv_layout(int64_t S, int32_t W, int64_t outer, int64_t inner, int64_t* counts,
+                         int64_t* displs) {
+  if (!counts || !displs) return fail(SP_EINVAL, "sp_allgatherv_layout: null output array");
+  if (W < 1) return fail(SP_EINVAL, "sp_allgatherv_layout: W must be >= 1 (got %d)", W);
+  if (S < 0 || outer < 0 || inner < 0)
+    return fail(SP_EINVAL, "sp_allgatherv_layout: S, outer and inner must be >= 0");
+  int64_t tot;
+  if (!mul_ok(outer, S, &tot) || !mul_ok(tot, inner, &tot))
+    return fail(SP_ERANGE, "sp_allgatherv_layout: outer*S*inner overflows int64");
+  int64_t off = 0;
+  for (int32_t r = 0; r < W; ++r) {
+    __int128 s = S;
+    int64_t a = static_cast<int64_t>((s * r) / W), b = static_cast<int64_t>((s * (r + 1)) / W);
+    counts[r] = outer * (b - a) * inner;  // <= tot, no overflow
+    displs[r] = off;
+    off += counts[r];
+  }
+  return ok();
+}
+
+int varlen_pack(int32_t dtype, int32_t W, const void* const* send, const int64_t* counts,
+                const int64_t* displs, void* flat, int64_t flat_elems, void* stream) {
+  const int eb = elem_bytes(dtype);
+  if (!eb) return fail(SP_EINVAL, "varlen_pack: unknown dtype %d", dtype);
+  if (W < 1) return fail(SP_EINVAL, "varlen_pack: W must be >= 1 (got %d)", W);
+  if (!send || !counts || !displs) return fail(SP_EINVAL, "varlen_pack: null host array");
+  if (flat_elems < 0) return fail(SP_EINVAL, "varlen_pack: flat_elems < 0");
+  int64_t flat_bytes;
+  if (!mul_ok(flat_elems, eb, &flat_bytes)) return fail(SP_ERANGE, "varlen_pack: flat size overflows");
+  std::vector<int64_t> sizes(W);
+  std::vector<CopySeg> segs;
+  for (int32_t r = 0; r < W; ++r) {
+    const int64_t c = counts[r], dsp = displs[r];
+    if (c < 0 || dsp < 0)
+      return fail(SP_EINVAL, "varlen_pack: rank %d has a negative count or displacement", r);
+    if (c > flat_elems || dsp > flat_elems - c)
+      return fail(SP_ERANGE, "varlen_pack: rank %d block [%lld, %lld) exceeds flat_elems %lld", r,
+                  (long long)dsp, (long long)dsp + (long long)c, (long long)flat_elems);
+    sizes[r] = c;
+    if (c == 0) continue;
+    if (!send[r]) return fail(SP_EINVAL, "varlen_pack: rank %d send pointer is null", r);
+    if (!flat) return fail(SP_EINVAL, "varlen_pack: flat is null");
+    if (ranges_overlap(send[r], c * eb, flat, flat_bytes))
+      return fail(SP_EOVERLAP, "varlen_pack: rank %d send buffer overlaps flat", r);
+    segs.push_back(CopySeg{static_cast<const char*>(send[r]), static_cast<char*>(flat) + dsp * eb,
+                           c * eb, 0, 0});
+  }
+  if (!blocks_disjoint(W, displs, sizes))
+    return fail(SP_EOVERLAP, "varlen_pack: destination blocks overlap");
+  return launch_copies(segs, 1, stream);
+}
+
+int varlen_unpack(int32_t dtype, int32_t W, const void* flat, int64_t flat_elems,
+                  const int64_t* displs, const int64_t* seq_lens, int64_t outer, int64_t inner,
+                  void* out, void* stream) {
+  const int eb = elem_bytes(dtype);
+  if (!eb) return fail(SP_EINVAL, "varlen_unpack: unknown dtype %d", dtype);
+  if (W < 1) return fail(SP_EINVAL, "varlen_unpack: W must be >= 1 (got %d)", W);
+  if (!displs || !seq_lens) return fail(SP_EINVAL, "varlen_unpack: null host array");
+  if (flat_elems < 0 || outer < 0 || inner < 0)
+    return fail(SP_EINVAL, "varlen_unpack: negative flat_elems, outer or inner");
+  int64_t flat_bytes;
+  if (!mul_ok(flat_elems, eb, &flat_bytes)) return fail(SP_ERANGE, "varlen_unpack: flat size overflows");
+  int64_t S = 0;
+  std::vector<int64_t> sizes(W);
+  for (int32_t r = 0; r < W; ++r) {
+    const int64_t s = seq_lens[r], dsp = displs[r];
+    if (s < 0 || dsp < 0)
+      return fail(SP_EINVAL, "varlen_unpack: rank %d has a negative length or displacement", r);
+    int64_t n;
+    if (!add_ok(S, s, &S) || !mul_ok(outer, s, &n) || !mul_ok(n, inner, &n))
+      return fail(SP_ERANGE, "varlen_unpack: sizes overflow int64");
+    if (n > flat_elems || dsp > flat_elems - n)
+      return fail(SP_ERANGE, "varlen_unpack: rank %d block [%lld, %lld) exceeds flat_elems %lld", r,
+                  (long long)dsp, (long long)dsp + (long long)n, (long long)flat_elems);
+    sizes[r] = n;
+  }
+  int64_t out_elems, out_bytes;
+  if (!mul_ok(outer, S, &out_elems) || !mul_ok(out_elems, inner, &out_elems) ||
+      !mul_ok(out_elems, eb, &out_bytes))
+    return fail(SP_ERANGE, "varlen_unpack: output size overflows int64");
+  if (!blocks_disjoint(W, displs, sizes))
+    return fail(SP_EOVERLAP, "varlen_unpack: source blocks overlap");
+  if (out_elems == 0) return ok();
+  if (!flat || !out) return fail(SP_EINVAL, "varlen_unpack: null device pointer");
+  if (ranges_overlap(out, out_bytes, flat, flat_bytes))
+    return fail(SP_EOVERLAP, "varlen_unpack: out overlaps flat");
+  std::vector<CopySeg> segs;
+  int64_t a = 0;
+  for (int32_t r = 0; r < W; ++r) {
+    const int64_t s = seq_lens[r];
+    if (s > 0 && inner > 0)
+      segs.push_back(CopySeg{static_cast<const char*>(flat) + displs[r] * eb,
+                             static_cast<char*>(out) + a * inner * eb, s * inner * eb,
+                             s * inner * eb, S * inner * eb});
+    a += s;
+  }
+  return launch_copies(segs, outer, stream);
+}
+
+int rope_apply(int32_t dtype, const void* x, void* y, int64_t s, int32_t H, int32_t d,
+               int64_t pos0, double theta, int32_t style, void* stream) {
+  const int eb = elem_bytes(dtype);
+  if (!eb) return fail(SP_EINVAL, "rope_apply: unknown dtype %d", dtype);
+  if (style != SP_ROPE_HALF && style != SP_ROPE_INTERLEAVED)
+    return fail(SP_EINVAL, "rope_apply: unknown style %d", style);
+  if (s < 0 || H < 1) return fail(SP_EINVAL, "rope_apply: need s >= 0 and H >= 1");
+  if (d < 2 || d > 1024 || (d & 1)) return fail(SP_EINVAL, "rope_apply: d must be even, 2..1024 (got %d)", d);
+  if (!(std::isfinite(theta) && theta > 0.0)) return fail(SP_EINVAL, "rope_apply: theta must be finite and > 0");
+  const int64_t lim = int64_t(1) << 53;
+  if (pos0 <= -lim || pos0 >= lim || pos0 + s >= lim)
+    return fail(SP_EINVAL, "rope_apply: positions must stay within +-2^53");
+  int64_t n, bytes;
+  if (!mul_ok(s, int64_t(H) * d, &n) || !mul_ok(n, eb, &bytes))
+    return fail(SP_ERANGE, "rope_apply: size overflows int64");
+  if (n == 0) return ok();
+  if (!x || !y) return fail(SP_EINVAL, "rope_apply: null device pointer");
+  if (x != y && ranges_overlap(x, bytes, y, bytes))
+    return fail(SP_EOVERLAP, "rope_apply: x and y overlap without being equal");
+  hipGetLastError();
+  hipError_t e = spattn::launch_rope(dtype, x, y, s, H, d, pos0, theta, style, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "rope launch");
+  return ok();
+}
+
+int shard_attn_fwd(int32_t dtype, const void* q, const void* k, const void* v, void* o, float* lse,
+                   int64_t sq, int64_t skv, int32_t H, int32_t d, float scale, void* stream) {
+  const int eb = elem_bytes(dtype);
+  if (!eb) return fail(SP_EINVAL, "shard_attn_fwd: unknown dtype %d", dtype);
+  if (sq < 0 || skv < 1 || H < 1) return fail(SP_EINVAL, "shard_attn_fwd: need sq >= 0, skv >= 1, H >= 1");
+  if (d != 64 && d != 128) return fail(SP_EUNSUPPORTED, "shard_attn_fwd: head size %d not supported (64, 128)", d);
+  if (!(std::isfinite(scale) && scale > 0.f)) return fail(SP_EINVAL, "shard_attn_fwd: scale must be finite and > 0");
+  int64_t qn, kn, qb, kb, lb;
+  if (!mul_ok(sq, int64_t(H) * d, &qn) || !mul_ok(skv, int64_t(H) * d, &kn) || !mul_ok(qn, eb, &qb) ||
+      !mul_ok(kn, eb, &kb) || !mul_ok(sq, int64_t(H) * 4, &lb))
+    return fail(SP_ERANGE, "shard_attn_fwd: size overflows int64");
+  // Grid: one work-group per (32-query tile, head) at most; keep it inside 2^31.
+  if ((sq + 31) / 32 > spattn::kMaxGrid / H)
+    return fail(SP_ERANGE, "shard_attn_fwd: sq*H too large for one launch");
+  if (skv > (int64_t(1) << 31) - 256) return fail(SP_ERANGE, "shard_attn_fwd: skv must be < 2^31");
+  if (sq == 0) return ok();
+  if (!q || !k || !v || !o) return fail(SP_EINVAL, "shard_attn_fwd: null device pointer");
+  if (ranges_overlap(o, qb, q, qb) || ranges_overlap(o, qb, k, kb) || ranges_overlap(o, qb, v, kb))
+    return fail(SP_EOVERLAP, "shard_attn_fwd: o overlaps an input");
+  if (lse && (ranges_overlap(lse, lb, q, qb) || ranges_overlap(lse, lb, k, kb) ||
+              ranges_overlap(lse, lb, v, kb) || ranges_overlap(lse, lb, o, qb)))
+    return fail(SP_EOVERLAP, "shard_attn_fwd: lse overlaps another buffer");
+  hipGetLastError();
+  hipError_t e;
+  if (dtype == SP_BF16)
+    e = spattn::launch_attn_bf16(q, k, v, o, lse, sq, skv, H, d, scale, as_stream(stream));
+  else
+    e = spattn::launch_attn_f32(static_cast<const float*>(q), static_cast<const float*>(k),
+                                static_cast<const float*>(v), static_cast<float*>(o), lse, sq, skv, H,
+                                d, scale, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,36 @@
+// Launchers shared between the host C ABI (capi.cpp) and the gfx950 kernels.
+// Arguments reaching these functions have been validated by capi.cpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace spattn {
+
+// One contiguous copy per (outer slice, segment):
+//   bytes [0, nbytes) of src + o*src_stride  ->  dst + o*dst_stride, o in [0, outer)
+struct CopySeg {
+  const char* src;
+  char* dst;
+  int64_t nbytes;
+  int64_t src_stride;
+  int64_t dst_stride;
+};
+
+// Enqueue the copies of `n` segments (any n >= 0) on `stream`.
+hipError_t launch_segcopy(const CopySeg* segs, int n, int64_t outer, hipStream_t stream);
+
+// RoPE of x[s, H, d] into y (may alias x).  dtype: 0 f32, 1 bf16.  style: 0 half, 1 interleaved.
+hipError_t launch_rope(int dtype, const void* x, void* y, int64_t s, int H, int d,
+                       int64_t pos0, double theta, int style, hipStream_t stream);
+
+// Attention of q[sq, H, d] against k, v[skv, H, d].
+hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int64_t sq, int64_t skv, int H, int d, float scale, hipStream_t stream);
+hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                           int64_t sq, int64_t skv, int H, int d, float scale, hipStream_t stream);
+
+// Largest grid (work-groups) the attention launchers accept.
+constexpr int64_t kMaxGrid = (int64_t(1) << 31) - 1;
+
+}  // namespace spattn

@@ -1,0 +1,99 @@
+"""One rank's share of packed-token sequence-parallel DiT attention on one GPU.
+
+The sequence of library calls that one rank makes, as the pages lay it out
+(MiniMax-H3-Comfy-NPU, sections 机制一 and 机制二/后端 A):
+  1. RoPE on the rank's local Q and K slice at absolute positions,
+  2. AllGatherV of K and V: every rank's shard packed into a flat buffer by
+     counts/displacements, then narrow/view/concat back to [S, H, d],
+  3. attention of the local Q against the full K/V,
+  4. the final AllGatherV of the per-rank outputs along the sequence.
+On one GPU the W ranks' shards are W separate device buffers; the other
+ranks' K shards are rotated once at set-up (each rank rotates its own), and
+their outputs are stand-in buffers of the right shape (their attention would
+run on their own GPUs).  Only library calls run here: no computation in
+Python, no synchronisation.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import api
+
+
+class RankShare:
+    def __init__(self, S: int, W: int, r: int, H: int, d: int, dtype: torch.dtype,
+                 theta: float = 10000.0, device="cuda", style: str = "half"):
+        self.S, self.W, self.r, self.H, self.d = S, W, r, H, d
+        self.dtype, self.theta, self.style, self.device = dtype, theta, style, torch.device(device)
+        self.bounds = [api.sp_shard_bounds(S, W, i) for i in range(W)]
+        self.lens = [b - a for a, b in self.bounds]
+        self.inner = H * d
+        self.counts, self.displs = api.sp_allgatherv_layout(S, W, 1, self.inner)
+        self.scale = 1.0 / math.sqrt(d)
+        a, b = self.bounds[r]
+        self.a, self.b = a, b
+        e = dict(dtype=dtype, device=self.device)
+        self.q_rot = torch.empty(b - a, H, d, **e)
+        self.k_rot = [torch.empty(n, H, d, **e) for n in self.lens]
+        self.flat_k = torch.empty(S * self.inner, **e)
+        self.flat_v = torch.empty(S * self.inner, **e)
+        self.k_full = torch.empty(S, H, d, **e)
+        self.v_full = torch.empty(S, H, d, **e)
+        self.o_shards = [torch.zeros(n, H, d, **e) for n in self.lens]
+        self.flat_o = torch.empty(S * self.inner, **e)
+        self.o_full = torch.empty(S, H, d, **e)
+        self.lse = torch.empty(H, b - a, dtype=torch.float32, device=self.device)
+        self.q = self.k = self.v = None
+
+    def set_inputs(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor) -> None:
+        """Full-sequence raw Q, K, V [S, H, d] on the device; rank shards are row slices."""
+        for t in (q, k, v):
+            if t.shape != (self.S, self.H, self.d) or t.dtype != self.dtype or not t.is_contiguous():
+                raise ValueError("inputs must be contiguous [S, H, d] of the share's dtype")
+        self.q, self.k, self.v = q, k, v
+        self.v_shards = [v[a:b] for a, b in self.bounds]
+        for i, (a, b) in enumerate(self.bounds):  # other ranks rotate their own K
+            if i != self.r:
+                api.rope_apply(k[a:b], a, self.theta, self.style, out=self.k_rot[i])
+
+    # -- the rank's hot path ------------------------------------------------------
+    def rope(self) -> None:
+        a, b = self.a, self.b
+        api.rope_apply(self.q[a:b], a, self.theta, self.style, out=self.q_rot)
+        api.rope_apply(self.k[a:b], a, self.theta, self.style, out=self.k_rot[self.r])
+
+    def gather_kv_pack(self) -> None:
+        api.varlen_pack([t.view(-1) for t in self.k_rot], self.counts, self.displs, self.flat_k)
+        api.varlen_pack([t.reshape(-1) for t in self.v_shards], self.counts, self.displs, self.flat_v)
+
+    def gather_kv_unpack(self) -> None:
+        api.varlen_unpack(self.flat_k, self.displs, self.lens, 1, self.inner, self.k_full)
+        api.varlen_unpack(self.flat_v, self.displs, self.lens, 1, self.inner, self.v_full)
+
+    def gather_kv(self) -> None:
+        self.gather_kv_pack()
+        self.gather_kv_unpack()
+
+    def attend(self) -> None:
+        api.shard_attn_fwd(self.q_rot, self.k_full, self.v_full, out=self.o_shards[self.r],
+                           lse=self.lse, scale=self.scale)
+
+    def concat_out(self) -> None:
+        api.varlen_pack([t.view(-1) for t in self.o_shards], self.counts, self.displs, self.flat_o)
+        api.varlen_unpack(self.flat_o, self.displs, self.lens, 1, self.inner, self.o_full)
+
+    def step(self) -> None:
+        self.rope()
+        self.gather_kv()
+        self.attend()
+        self.concat_out()
+
+    # -- algorithmic work of one step -------------------------------------------------
+    def attn_flops(self) -> int:
+        return 4 * (self.b - self.a) * self.S * self.H * self.d
+
+    def pack_kv_bytes(self) -> int:
+        """Read + write bytes of the K and V pack (one AllGatherV of each)."""
+        return 2 * 2 * self.S * self.inner * self.flat_k.element_size()

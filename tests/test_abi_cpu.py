@@ -1,0 +1,129 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+include/spattn.h declares, the host-only entry points agree bit-exactly with
+the oracle, and every argument error is reported before anything is enqueued.
+(Entry points that compute on the device are only called here with arguments
+that fail validation, so no HIP work is ever started.)"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+from sequence_dit_attention_amd import _lib
+from sequence_dit_attention_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spattn.h")
+
+SP_EINVAL, SP_EUNSUPPORTED, SP_ERANGE, SP_EOVERLAP = -1, -2, -3, -4
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert "shard_attn_fwd" in names and len(names) == 8
+    h = ctypes.CDLL(_lib.LIB_PATH)
+    for n in names:
+        assert hasattr(h, n), n
+    assert sorted(n for n, _, _ in _lib.SIGNATURES) == names
+    assert api.sp_abi_version() == 1
+
+
+def test_shard_bounds_match_oracle():
+    for S in list(range(0, 300)) + [16383, 25640, 125117, 367287, 2**62 + 5]:
+        for W in (1, 2, 3, 4, 7, 8, 16):
+            for r in range(W):
+                assert api.sp_shard_bounds(S, W, r) == oracle.shard_bounds(S, W, r)
+
+
+def test_layout_matches_oracle():
+    for S, W, outer, inner in [(16383, 4, 1, 2048), (1001, 4, 1, 128), (7, 4, 3, 5), (3, 8, 2, 1)]:
+        assert api.sp_allgatherv_layout(S, W, outer, inner) == oracle.allgatherv_layout(S, W, outer, inner)
+
+
+def _code(fn, *args):
+    return fn(*args)
+
+
+def test_host_errors():
+    L = _lib.lib()
+    a, b = ctypes.c_int64(), ctypes.c_int64()
+    assert L.sp_shard_bounds(10, 0, 0, ctypes.byref(a), ctypes.byref(b)) == SP_EINVAL
+    assert L.sp_shard_bounds(10, 4, 4, ctypes.byref(a), ctypes.byref(b)) == SP_EINVAL
+    assert L.sp_shard_bounds(-1, 4, 0, ctypes.byref(a), ctypes.byref(b)) == SP_EINVAL
+    assert L.sp_shard_bounds(10, 4, 0, None, ctypes.byref(b)) == SP_EINVAL
+    assert b"rank" in L.sp_last_error() or b"null" in L.sp_last_error()
+    c, d = (ctypes.c_int64 * 4)(), (ctypes.c_int64 * 4)()
+    assert L.sp_allgatherv_layout(2**40, 4, 2**20, 2**10, c, d) == SP_ERANGE
+    assert L.sp_allgatherv_layout(10, 4, -1, 1, c, d) == SP_EINVAL
+    assert L.sp_shard_bounds(10, 4, 1, ctypes.byref(a), ctypes.byref(b)) == 0
+    assert L.sp_last_error() == b""
+
+
+def _arr(vals, t=ctypes.c_int64):
+    return (t * len(vals))(*vals)
+
+
+FAKE = 1 << 40  # never dereferenced: every call below fails validation first
+
+
+def test_pack_validation():
+    L = _lib.lib()
+    ptrs = (ctypes.c_void_p * 2)(FAKE, FAKE + 10_000)
+    cnt, dsp = _arr([4, 4]), _arr([0, 4])
+    assert L.varlen_pack(7, 2, ptrs, cnt, dsp, FAKE * 2, 8, None) == SP_EINVAL          # dtype
+    assert L.varlen_pack(1, 0, ptrs, cnt, dsp, FAKE * 2, 8, None) == SP_EINVAL          # W
+    assert L.varlen_pack(1, 2, ptrs, _arr([-1, 4]), dsp, FAKE * 2, 8, None) == SP_EINVAL
+    assert L.varlen_pack(1, 2, ptrs, cnt, _arr([0, 5]), FAKE * 2, 8, None) == SP_ERANGE  # past end
+    assert L.varlen_pack(1, 2, ptrs, cnt, _arr([0, 3]), FAKE * 2, 8, None) == SP_EOVERLAP
+    assert L.varlen_pack(1, 2, (ctypes.c_void_p * 2)(FAKE, None), cnt, dsp, FAKE * 2, 8, None) == SP_EINVAL
+    # source overlapping the destination
+    assert L.varlen_pack(1, 2, (ctypes.c_void_p * 2)(FAKE, FAKE * 2 + 4), cnt, dsp, FAKE * 2, 8, None) == SP_EOVERLAP
+    assert b"overlap" in L.sp_last_error()
+
+
+def test_unpack_validation():
+    L = _lib.lib()
+    dsp, lens = _arr([0, 6]), _arr([2, 2])
+    assert L.varlen_unpack(9, 2, FAKE, 12, dsp, lens, 1, 3, FAKE * 2, None) == SP_EINVAL
+    assert L.varlen_unpack(1, 2, FAKE, 11, dsp, lens, 1, 3, FAKE * 2, None) == SP_ERANGE
+    assert L.varlen_unpack(1, 2, FAKE, 12, _arr([0, 5]), lens, 1, 3, FAKE * 2, None) == SP_EOVERLAP
+    assert L.varlen_unpack(1, 2, FAKE, 12, dsp, _arr([2, -2]), 1, 3, FAKE * 2, None) == SP_EINVAL
+    assert L.varlen_unpack(1, 2, FAKE, 12, dsp, lens, 1, 3, FAKE + 4, None) == SP_EOVERLAP
+
+
+def test_rope_validation():
+    L = _lib.lib()
+    assert L.rope_apply(1, FAKE, FAKE, 10, 2, 7, 0, 1e4, 0, None) == SP_EINVAL      # odd d
+    assert L.rope_apply(1, FAKE, FAKE, 10, 2, 8, 0, -1.0, 0, None) == SP_EINVAL     # theta
+    assert L.rope_apply(1, FAKE, FAKE, 10, 2, 8, 0, 1e4, 5, None) == SP_EINVAL      # style
+    assert L.rope_apply(1, FAKE, FAKE, 10, 0, 8, 0, 1e4, 0, None) == SP_EINVAL      # H
+    assert L.rope_apply(1, FAKE, FAKE, 10, 2, 8, 2**53, 1e4, 0, None) == SP_EINVAL  # positions
+    assert L.rope_apply(1, FAKE, FAKE + 2, 10, 2, 8, 0, 1e4, 0, None) == SP_EOVERLAP
+
+
+def test_attn_validation():
+    L = _lib.lib()
+    f = L.shard_attn_fwd
+    q, k, v, o = FAKE, FAKE * 2, FAKE * 3, FAKE * 4
+    assert f(1, q, k, v, o, None, 10, 20, 2, 96, 0.1, None) == SP_EUNSUPPORTED
+    assert f(3, q, k, v, o, None, 10, 20, 2, 128, 0.1, None) == SP_EINVAL
+    assert f(1, q, k, v, o, None, 10, 0, 2, 128, 0.1, None) == SP_EINVAL
+    assert f(1, q, k, v, o, None, 10, 20, 2, 128, 0.0, None) == SP_EINVAL
+    assert f(1, q, k, v, o, None, 10, 20, 2, 128, float("nan"), None) == SP_EINVAL
+    assert f(1, q, k, v, q + 64, None, 10, 20, 2, 128, 0.1, None) == SP_EOVERLAP
+    assert f(1, q, k, v, o, o + 8, 10, 20, 2, 128, 0.1, None) == SP_EOVERLAP
+    assert f(1, None, k, v, o, None, 10, 20, 2, 128, 0.1, None) == SP_EINVAL
+    assert f(1, q, k, v, o, None, 0, 20, 2, 128, 0.1, None) == 0   # sq == 0: nothing enqueued
+
+
+def test_python_wrapper_raises():
+    with pytest.raises(_lib.SpattnError) as ei:
+        api.sp_shard_bounds(5, 2, 2)
+    assert ei.value.code == SP_EINVAL
