@@ -164,7 +164,8 @@ int rope_apply(int32_t dtype, const void* x, void* y, int64_t s, int32_t H, int3
  * row's result does not depend on sq or on where the row sits in q.
  * Errors: SP_EINVAL (bad dtype, sq < 0, skv < 1, H < 1, scale not finite or
  * <= 0, null pointers with data), SP_EUNSUPPORTED (d not 64 or 128),
- * SP_ERANGE (sizes beyond the kernel's 32-bit grid), SP_EOVERLAP (o or lse
+ * SP_ERANGE (sizes beyond the kernel's 32-bit grid, or 64 tokens of K spanning
+ * 2 GiB or more), SP_EOVERLAP (o or lse
  * overlaps an input or each other), SP_EHIP.  sq == 0 enqueues nothing.
  */
 int shard_attn_fwd(int32_t dtype, const void* q, const void* k, const void* v,

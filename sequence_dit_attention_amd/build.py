@@ -31,13 +31,21 @@ COMMON = [
 ]
 
 
+# Per-file flags.  The attention kernel keeps every MFMA operand and result in
+# VGPRs (the scores feed VALU softmax code; AGPR copies would cost more than
+# they save) and needs no NaN canonicalisation before its max reductions.
+EXTRA = {
+    "attn_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true", "-fno-honor-nans"],
+}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON, "-x", "hip", "-c", src, "-o", obj]
+    cmd = [HIPCC, *COMMON, *EXTRA.get(os.path.basename(src), []), "-x", "hip", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

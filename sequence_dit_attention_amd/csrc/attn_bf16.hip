@@ -5,23 +5,38 @@
 // is passed in (page "NPU HunyuanImage-3.0模型推理优化实践", 消除FA中scale的冗余计算).
 //
 // Design (MI355X / CDNA4):
-//  * One work-group = 4 waves = BM query rows of one head; each wave owns
-//    32*QB rows whose Q fragments stay in VGPRs for the whole key loop.
-//  * Keys stream through LDS in tiles of 64 (K and V, double buffered, 16-byte
-//    chunks XOR-swizzled per row so MFMA operand reads spread over the banks).
+//  * One work-group = 4 waves (one per SIMD) = 256 query rows of one head; each
+//    wave owns 64 rows (two 32-column MFMA blocks), whose Q fragments stay in
+//    VGPRs for the whole key loop.  Two query blocks per wave halve the LDS
+//    operand reads per MFMA flop, which bound a 32-row-per-wave layout.
+//  * Keys stream through LDS in tiles of 64, K and V double buffered, filled
+//    by global_load_lds_dwordx4 straight from HBM/L2 (no VGPR staging).  Each
+//    row's 16-byte chunks are XOR-swizzled; because an LDS-direct load writes
+//    lane i at base + 16*i, the swizzle is applied to the global addresses.
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //    a lane then holds 16 keys of ONE query column, so the softmax max and sum
-//    are lane-local except for one exchange between the two wave halves.
+//    are lane-local except for one v_permlane32_swap between wave halves.
 //  * The probabilities are converted to bf16 in place (v_cvt_pk_bf16_f32) and
-//    feed O^T += V^T P^T directly as the MFMA B operand; the matching V^T
-//    operand is read from the row-major V tile with the gfx950 transposing LDS
-//    read ds_read_b64_tr_b16.  The k index of that MFMA is a permutation of
-//    the keys (the layout the S^T accumulator already has); the same
-//    permutation is applied to V, so the contraction is unchanged.
-//  * Online softmax in float32, base 2, scale folded into log2(e).
-//  * Work-group ids are remapped so that the work-groups resident on one XCD
-//    (dispatch is round-robin over the 8 XCDs) work on neighbouring query
-//    tiles of the same head and share that head's K/V stream in their L2.
+//    feed O^T += V^T P^T as the MFMA B operand; the V^T operand is read from
+//    the row-major V tile with the transposing LDS read ds_read_b64_tr_b16.
+//    The k index of that MFMA is a permutation of the keys (the order in
+//    which the S^T accumulator holds them); V is read in the same order, so
+//    the contraction is unchanged.
+//  * Online softmax in float32, base 2, scale folded into log2(e).  The
+//    running maximum is only raised when a tile's maximum exceeds it by more
+//    than kTau (a factor 2^8): probabilities then stay <= 2^8, harmless in
+//    float32 sums and bf16 operands, and the O rescale (a wave-uniform
+//    branch) runs a handful of times per row instead of every tile.  The
+//    result O = sum(p v) / sum(p) does not depend on the reference maximum.
+//    Row sums add the bf16 probabilities the P*V product uses (v_dot2 with
+//    ones), so O is normalised by exactly the weights it was built from.
+//  * Software pipeline: while the softmax of tile t runs on the VALU, the
+//    MFMAs already compute S^T of tile t+1 (independent registers), then P*V
+//    of tile t follows.  The loop is unrolled by two so the two S^T register
+//    sets alternate roles without copies.
+//  * Work-groups are ordered head-major, so at any time all XCDs work on the
+//    same head: its K+V (188 MB at 367k tokens) stays in the 256 MB Infinity
+//    Cache and each XCD's L2 serves its co-resident query tiles.
 // Per output row the arithmetic depends only on that query row and on K/V in
 // a fixed key order, so results are deterministic and independent of sq and
 // of the row's position inside a tile.
@@ -38,30 +53,41 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kBN = 64;         // keys per tile
-constexpr int kKB = kBN / 32;   // 32-key blocks per tile
+constexpr int QB = 2;                  // 32-query MFMA blocks per wave
+constexpr int BM = kWaves * 32 * QB;   // query rows per work-group
+constexpr int kBN = 64;                // keys per tile
+constexpr int kKB = kBN / 32;          // 32-key blocks per tile
+constexpr float kTau = 8.0f;           // lazy-rescale threshold (log2 units)
 constexpr float kLn2 = 0.69314718055994531f;
 
 template <int D>
 struct Geo {
-  static constexpr int kCh = D / 8;                      // 16-byte chunks per K/V row
-  static constexpr int kDC = D / 16;                     // k-steps of the Q.K MFMA
-  static constexpr int kND = D / 32;                     // 32-row d-blocks of O^T
-  static constexpr int kRowB = D * 2;                    // bytes per K/V row
-  static constexpr int kTileB = kBN * kRowB;             // bytes per K or V tile
-  static constexpr int kStage = kBN * kCh / kThreads;    // 16-byte chunks per lane per tile
-  // K rows: chunk c of row r lives at c ^ (r mod kCh): the 32 rows one
-  // MFMA operand read touches land on distinct chunk columns.
-  static __device__ int swz_k(int r, int c) { return c ^ (r & (kCh - 1)); }
+  static constexpr int kCh = D / 8;                       // 16-byte chunks per K/V row
+  static constexpr int kDC = D / 16;                      // k-steps of the Q.K MFMA
+  static constexpr int kND = D / 32;                      // 32-row d-blocks of O^T
+  static constexpr int kRowB = D * 2;                     // bytes per K/V row
+  static constexpr int kTileB = kBN * kRowB;              // bytes per K or V tile
+  static constexpr int kLoads = kTileB / (kThreads * 16); // LDS-direct loads per lane per tile
+  // K rows: chunk c of row r lives at c ^ (r mod kCh): the 32 rows an MFMA
+  // operand read touches land on distinct chunk columns.
+  static __device__ int swz_k(int r) { return r & (kCh - 1); }
   // V rows: the transposing read takes 4 rows x 32 bytes per 16 lanes; XOR
   // with 4*(r mod kCh/4) moves those rows to different 64-byte bank groups.
-  static __device__ int swz_v(int r, int c) { return c ^ ((r & (kCh / 4 - 1)) << 2); }
+  static __device__ int swz_v(int r) { return (r & (kCh / 4 - 1)) << 2; }
 };
 
-__device__ inline float other_half(float x) { return __shfl_xor(x, 32); }
+__device__ inline float other_half_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+}
+__device__ inline float halves_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
 
 __device__ inline uint32_t pack_bf16x2(float a, float b) {
   f32x2 f = {a, b};
@@ -69,30 +95,298 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
-template <int D, int QB>
+// ---- K/V tile loads: LDS-direct buffer loads.  Wave w fills 1 KiB blocks
+// w*kLoads .. w*kLoads+kLoads-1 of a 64-row tile; lane i of a load writes
+// bytes [16i, 16i+16) of its block, so the per-lane source offsets (row, and
+// the chunk that the XOR swizzle maps to that position) are fixed for the
+// whole kernel and only the tile base (scalar) moves.
+template <int D, bool IS_V>
+struct TileLoader {
+  using G = Geo<D>;
+  uint32_t voff[G::kLoads];  // byte offset of this lane's chunk from the tile's first row
+  int rows[G::kLoads];       // tile row this lane loads
+
+  __device__ void init(int wave, int lane, int64_t rowbytes) {
+#pragma unroll
+    for (int i = 0; i < G::kLoads; ++i) {
+      const int byte = (wave * G::kLoads + i) * 1024 + lane * 16;
+      const int r = byte / G::kRowB;
+      const int p = (byte % G::kRowB) >> 4;
+      const int c = p ^ (IS_V ? G::swz_v(r) : G::swz_k(r));
+      rows[i] = r;
+      voff[i] = uint32_t(r * rowbytes + c * 16);
+    }
+  }
+  // Full tile: every row < skv.
+  __device__ void load(const uint16_t* hb, int tile, int64_t rowbytes, char* lds, int wave) const {
+    const char* base = reinterpret_cast<const char*>(hb) + int64_t(tile) * kBN * rowbytes;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, 0x7FFFFFFF, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < G::kLoads; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + (wave * G::kLoads + i) * 1024), 16, voff[i],
+                                               0, 0, 0);
+  }
+  // Last tile of a ragged sequence: rows >= skv re-read row skv-1 (finite data;
+  // those keys are masked to -inf, so they carry zero weight).
+  __device__ void load_clamped(const uint16_t* hb, int tile, int skv, int64_t rowbytes, char* lds,
+                               int wave) const {
+    const char* base = reinterpret_cast<const char*>(hb) + int64_t(tile) * kBN * rowbytes;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, 0x7FFFFFFF, 0x00020000);
+    const int valid = skv - tile * kBN;
+#pragma unroll
+    for (int i = 0; i < G::kLoads; ++i) {
+      const int over = rows[i] >= valid ? rows[i] - (valid - 1) : 0;
+      const uint32_t off = voff[i] - uint32_t(over * rowbytes);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + (wave * G::kLoads + i) * 1024), 16, off, 0,
+                                               0, 0);
+    }
+  }
+};
+
+// S^T of 32 keys (rows r0 .. r0+31 of an LDS K tile) against the wave's 64
+// queries.  MASKED: accumulated onto `init` (-inf on keys past the end of the
+// sequence, else 0); otherwise onto the inline constant 0.
+template <int D, bool MASKED>
+__device__ inline void qk32(f32x16 (&s)[QB], const char* kb, int r0, const bf16x8 (&qf)[QB][Geo<D>::kDC],
+                            const f32x16& init, int col, int hf) {
+  using G = Geo<D>;
+  const int r = r0 + col;
+  const char* rowp = kb + r * G::kRowB;
+  const int sw = G::swz_k(r);
+#pragma unroll
+  for (int cc = 0; cc < G::kDC; ++cc) {
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(rowp + (((2 * cc + hf) ^ sw) << 4));
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      if (cc > 0)
+        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][cc], s[qb], 0, 0, 0);
+      else if (MASKED)
+        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][cc], init, 0, 0, 0);
+      else
+        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][cc], f32x16{}, 0, 0, 0);
+    }
+  }
+}
+
+// Accumulator init for keys key0 .. key0+31: -inf where key >= skv, else 0.
+__device__ inline f32x16 tail_init(int key0, int skv, int hf) {
+  f32x16 m;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) m[r] = (key0 + 8 * (r >> 2) + 4 * hf + (r & 3) >= skv) ? -INFINITY : 0.f;
+  return m;
+}
+
+// Softmax state of the wave's 64 query columns (both wave halves hold the same values).
+struct SoftState {
+  float m_run[QB];  // reference maximum (log2 units) the probabilities are taken against
+  float l_run[QB];  // this lane's partial sum of bf16 probabilities
+  float alpha[QB];  // factor taking the accumulators from the previous to the current reference
+  bool any;         // some column's reference moved: O must be scaled by alpha
+};
+
+// Maximum of a 32-key block; raises the reference maximum of every column of
+// the wave when any column's block maximum exceeds its reference by > kTau.
+__device__ inline void block_max(const f32x16 (&s)[QB], SoftState& st, float c) {
+  float mt[QB];
+  bool need = false;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    float mx = fmaxf(s[qb][0], s[qb][1]);
+#pragma unroll
+    for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[qb][r], s[qb][r + 1]));
+    mt[qb] = other_half_max(mx) * c;
+    need |= mt[qb] > st.m_run[qb] + kTau;
+  }
+  st.any = __builtin_amdgcn_ballot_w64(need) != 0;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float m_new = st.any ? fmaxf(st.m_run[qb], mt[qb]) : st.m_run[qb];
+    st.alpha[qb] = __builtin_amdgcn_exp2f(st.m_run[qb] - m_new);
+    st.m_run[qb] = m_new;
+  }
+}
+
+// Probabilities of a 32-key block as packed bf16 pairs: pw[qb][u][e] holds
+// keys (8u + 2e, 8u + 2e + 1) of the lane's accumulator order; pw[qb][u][0..3]
+// is the B operand of P*V MFMA u.  (Kept as plain 32-bit words: element
+// extraction from a vector type under __builtin_bit_cast was miscompiled.)
+typedef uint32_t PW[QB][2][4];
+
+// p = 2^(s*c - m) rounded to bf16 pairs: the B operands of P*V.
+__device__ inline void probs(const f32x16 (&s)[QB], PW& pb, const SoftState& st, float c) {
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[qb][8 * u + 2 * e], c, -st.m_run[qb]));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[qb][8 * u + 2 * e + 1], c, -st.m_run[qb]));
+        pb[qb][u][e] = pack_bf16x2(p0, p1);
+      }
+}
+
+// l = l * alpha + sum of the bf16 probabilities (v_dot2 against ones).
+__device__ inline void row_sums(const PW& pb, SoftState& st) {
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    float ls = st.l_run[qb] * st.alpha[qb];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pb[qb][u][e]), ones, ls, false);
+    st.l_run[qb] = ls;
+  }
+}
+
+template <int D>
+__device__ inline void rescale_o(f32x16 (&o)[Geo<D>::kND][QB], const float (&alpha)[QB]) {
+#pragma unroll
+  for (int db = 0; db < Geo<D>::kND; ++db)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][qb][r] *= alpha[qb];
+}
+
+// O^T += V^T P^T over the 32 keys at rows r0 .. r0+31 of an LDS V tile.  MFMA u
+// contracts keys r0 + 16u + {4hf..4hf+3, 8+4hf..8+4hf+3} in k-slots 8hf..8hf+7,
+// the order in which the S^T accumulator holds them.
+template <int D>
+__device__ inline void pv32(f32x16 (&o)[Geo<D>::kND][QB], const PW& pb, const char* vb, int r0, int lane,
+                            int hf) {
+  using G = Geo<D>;
+  const int g16 = lane >> 4, j16 = lane & 15;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int ra = r0 + 16 * u + 4 * hf + (j16 >> 2);
+#pragma unroll
+    for (int db = 0; db < G::kND; ++db) {
+      const int dcol = db * 32 + 16 * (g16 & 1) + 4 * (j16 & 3);
+      const int ch = dcol >> 3, inb = (dcol & 7) * 2;
+      const char* p0 = vb + ra * G::kRowB + ((ch ^ G::swz_v(ra)) << 4) + inb;
+      const char* p1 = vb + (ra + 8) * G::kRowB + ((ch ^ G::swz_v(ra + 8)) << 4) + inb;
+      const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
+      const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p1);
+      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            a, __builtin_bit_cast(bf16x8, u32x4{pb[qb][u][0], pb[qb][u][1], pb[qb][u][2], pb[qb][u][3]}),
+            o[db][qb], 0, 0, 0);
+    }
+  }
+}
+
+// Instruction-group masks of __builtin_amdgcn_sched_group_barrier.
+// (VALU excludes transcendental instructions, which have their own mask.)
+constexpr int kSgVALU = 0x002, kSgMFMA = 0x008, kSgDSRead = 0x100, kSgTrans = 0x400;
+
+// One 32-key step.  On entry `cur` holds S^T of the step's keys and `st` its
+// reference maximum (block_max already applied).  Region A: the MFMAs compute
+// S^T of the next 32 keys into `nxt` while the VALU turns `cur` into bf16
+// probabilities.  Region B: the MFMAs accumulate P*V while the VALU adds the
+// row sums and takes the maximum of `nxt`.  Both regions are branch-free so
+// the scheduler can interleave MFMA and VALU work as the groups below ask.
+template <int D, bool HAS_NEXT, bool MASK_NEXT>
+__device__ inline void step32(f32x16 (&cur)[QB], f32x16 (&nxt)[QB], SoftState& st, PW& pb,
+                              f32x16 (&acc)[Geo<D>::kND][QB], const bf16x8 (&qf)[QB][Geo<D>::kDC],
+                              const char* kb_next, int rk_next, const f32x16& init_next, const char* vb, int rv,
+                              float c, int lane, int col, int hf) {
+  using G = Geo<D>;
+  if (st.any) rescale_o<D>(acc, st.alpha);
+  __builtin_amdgcn_sched_barrier(0);
+  // region A: 16 MFMAs (with the 8 K-fragment reads two groups ahead) and the
+  // 32 exponentials + 48 other VALU instructions of the probabilities.
+  if (HAS_NEXT) qk32<D, MASK_NEXT>(nxt, kb_next, rk_next, qf, init_next, col, hf);
+  probs(cur, pb, st, c);
+  if (HAS_NEXT) {
+    __builtin_amdgcn_sched_group_barrier(kSgDSRead, 2, 0);
+#pragma unroll
+    for (int i = 0; i < G::kDC; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSgMFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgVALU, 3, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgTrans, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgMFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgVALU, 3, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgTrans, 2, 0);
+      if (i + 2 < G::kDC) __builtin_amdgcn_sched_group_barrier(kSgDSRead, 1, 0);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // region B: 16 MFMAs (V^T fragments read two pairs ahead), row sums and the
+  // maximum of the next block.
+  pv32<D>(acc, pb, vb, rv, lane, hf);
+  row_sums(pb, st);
+  if (HAS_NEXT) block_max(nxt, st, c);
+  __builtin_amdgcn_sched_group_barrier(kSgDSRead, 4, 1);
+#pragma unroll
+  for (int i = 0; i < 2 * G::kND; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSgMFMA, 1, 1);
+    __builtin_amdgcn_sched_group_barrier(kSgVALU, 2, 1);
+    __builtin_amdgcn_sched_group_barrier(kSgMFMA, 1, 1);
+    __builtin_amdgcn_sched_group_barrier(kSgVALU, 2, 1);
+    if (i + 2 < 2 * G::kND) __builtin_amdgcn_sched_group_barrier(kSgDSRead, 2, 1);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+__device__ inline void wait_loads_and_barrier() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's LDS-direct loads have landed
+  __syncthreads();
+}
+
+template <int D>
 __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    uint16_t* __restrict__ o, float* __restrict__ lse, int sq, int skv, int H, float c,
-    int nqt, int nwg, int per_xcd) {
+    uint16_t* __restrict__ o, float* __restrict__ lse, int sq, int skv, int H, float c, int nqt) {
   using G = Geo<D>;
-  constexpr int BM = kWaves * 32 * QB;
-  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * G::kTileB];
+  // K tiles triple buffered (tile t is still read while tile t+2 streams in), V double.
+  __shared__ __attribute__((aligned(1024))) char smem[5 * G::kTileB];
+  char* const vbase = smem + 3 * G::kTileB;
 
-  // XCD-aware remap: hardware block b runs on XCD b % 8.
-  const int b = blockIdx.x;
-  const int L = (b & 7) * per_xcd + (b >> 3);
-  if (L >= nwg) return;
+  // Head-major order: consecutive work-groups (spread over all XCDs) share a head.
+  const int L = blockIdx.x;
   const int h = L / nqt;
   const int qt = L - h * nqt;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int col = lane & 31;   // query column inside a 32-block / row inside an MFMA A operand
-  const int hf = lane >> 5;    // wave half
-  const int64_t rowstride = int64_t(H) * D;  // elements between consecutive tokens
+  const int col = lane & 31;
+  const int hf = lane >> 5;
+  const int64_t rowstride = int64_t(H) * D;
+  const int64_t rowbytes = rowstride * 2;
+  const uint16_t* kh = k + int64_t(h) * D;
+  const uint16_t* vh = v + int64_t(h) * D;
+  const int nT = (skv + kBN - 1) / kBN;
+  const bool ragged = (skv % kBN) != 0;
 
-  // ---- Q fragments (B operand of S^T = K Q^T): lane holds 8 d-values of one query.
+  TileLoader<D, false> kl;
+  TileLoader<D, true> vl;
+  kl.init(wave, lane, rowbytes);
+  vl.init(wave, lane, rowbytes);
+  auto load_k = [&](int tile, int slot) {
+    char* dst = smem + slot * G::kTileB;
+    if (ragged && tile == nT - 1) kl.load_clamped(kh, tile, skv, rowbytes, dst, wave);
+    else kl.load(kh, tile, rowbytes, dst, wave);
+  };
+  auto load_v = [&](int tile, int slot) {
+    char* dst = vbase + slot * G::kTileB;
+    if (ragged && tile == nT - 1) vl.load_clamped(vh, tile, skv, rowbytes, dst, wave);
+    else vl.load(vh, tile, rowbytes, dst, wave);
+  };
+
+  // K tiles 0 and 1 and V tile 0 start streaming while Q is loaded.
+  load_k(0, 0);
+  load_k(min(1, nT - 1), 1);
+  load_v(0, 0);
+
+  // Q fragments (B operand of S^T = K Q^T): lane holds 8 d-values of one query.
   bf16x8 qf[QB][G::kDC];
   const int qrow0 = qt * BM + wave * 32 * QB;
 #pragma unroll
@@ -106,166 +400,70 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(
     }
   }
 
-  f32x16 acc_o[G::kND][QB];
+  f32x16 acc[G::kND][QB];
 #pragma unroll
   for (int db = 0; db < G::kND; ++db)
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc_o[db][qb][r] = 0.f;
-  float m_run[QB], l_run[QB];
+      for (int r = 0; r < 16; ++r) acc[db][qb][r] = 0.f;
+  SoftState st;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    m_run[qb] = -INFINITY;
-    l_run[qb] = 0.f;
+    st.m_run[qb] = -INFINITY;
+    st.l_run[qb] = 0.f;
+  }
+  const f32x16 zero = {};
+  const int last0 = (nT - 1) * kBN;  // first key of the last tile
+
+  f32x16 sa[QB], sb[QB];  // S^T of the current / next 32 keys
+  PW pb;
+
+  wait_loads_and_barrier();
+  if (nT == 1) qk32<D, true>(sa, smem, 0, qf, tail_init(0, skv, hf), col, hf);
+  else qk32<D, false>(sa, smem, 0, qf, zero, col, hf);
+  block_max(sa, st, c);
+
+  // Tile t (64 keys) = two 32-key steps.  Loads for K(t+2) and V(t+1) go to
+  // the buffers tile t-1 released (tile index clamped at the end).
+  int kcur = 0;  // LDS slot of K tile t (slots rotate mod 3)
+  auto tile_top = [&](int t) {
+    const int knext = kcur == 2 ? 0 : kcur + 1;
+    const int kfree = knext == 2 ? 0 : knext + 1;
+    wait_loads_and_barrier();
+    load_k(min(t + 2, nT - 1), kfree);
+    load_v(min(t + 1, nT - 1), (t + 1) & 1);
+    return knext;
+  };
+  int t = 0;
+  for (; t < nT - 2; ++t) {  // the next tile is not the last one: no masking
+    const int knext = tile_top(t);
+    const char* vb = vbase + (t & 1) * G::kTileB;
+    step32<D, true, false>(sa, sb, st, pb, acc, qf, smem + kcur * G::kTileB, 32, zero, vb, 0, c, lane, col, hf);
+    step32<D, true, false>(sb, sa, st, pb, acc, qf, smem + knext * G::kTileB, 0, zero, vb, 32, c, lane, col, hf);
+    kcur = knext;
+  }
+  if (t == nT - 2) {  // the next tile is the last one
+    const int knext = tile_top(t);
+    const char* vb = vbase + (t & 1) * G::kTileB;
+    step32<D, true, false>(sa, sb, st, pb, acc, qf, smem + kcur * G::kTileB, 32, zero, vb, 0, c, lane, col, hf);
+    step32<D, true, true>(sb, sa, st, pb, acc, qf, smem + knext * G::kTileB, 0, tail_init(last0, skv, hf), vb, 32,
+                          c, lane, col, hf);
+    kcur = knext;
+    ++t;
+  }
+  {  // last tile
+    wait_loads_and_barrier();
+    const char* vb = vbase + (t & 1) * G::kTileB;
+    step32<D, true, true>(sa, sb, st, pb, acc, qf, smem + kcur * G::kTileB, 32, tail_init(last0 + 32, skv, hf), vb,
+                          0, c, lane, col, hf);
+    step32<D, false, false>(sb, sa, st, pb, acc, qf, nullptr, 0, zero, vb, 32, c, lane, col, hf);
   }
 
-  // ---- K/V staging: global -> VGPRs -> LDS, one tile ahead.
-  const uint16_t* kh = k + int64_t(h) * D;
-  const uint16_t* vh = v + int64_t(h) * D;
-  u32x4 stk[G::kStage], stv[G::kStage];
-  auto stage_load = [&](int t) {
-    const int kv0 = t * kBN;
-#pragma unroll
-    for (int i = 0; i < G::kStage; ++i) {
-      const int cidx = tid + i * kThreads;
-      const int r = cidx / G::kCh, cch = cidx % G::kCh;
-      const int j = kv0 + r;
-      if (j < skv) {
-        stk[i] = *reinterpret_cast<const u32x4*>(kh + int64_t(j) * rowstride + cch * 8);
-        stv[i] = *reinterpret_cast<const u32x4*>(vh + int64_t(j) * rowstride + cch * 8);
-      } else {
-        stk[i] = u32x4{0, 0, 0, 0};
-        stv[i] = u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto stage_store = [&](int buf) {
-    char* kb = smem + buf * 2 * G::kTileB;
-    char* vb = kb + G::kTileB;
-#pragma unroll
-    for (int i = 0; i < G::kStage; ++i) {
-      const int cidx = tid + i * kThreads;
-      const int r = cidx / G::kCh, cch = cidx % G::kCh;
-      *reinterpret_cast<u32x4*>(kb + r * G::kRowB + G::swz_k(r, cch) * 16) = stk[i];
-      *reinterpret_cast<u32x4*>(vb + r * G::kRowB + G::swz_v(r, cch) * 16) = stv[i];
-    }
-  };
-
-  const int nT = (skv + kBN - 1) / kBN;
-  stage_load(0);
-  stage_store(0);
-  __syncthreads();
-
-  for (int t = 0; t < nT; ++t) {
-    const int buf = t & 1;
-    const bool more = t + 1 < nT;
-    if (more) stage_load(t + 1);
-    const char* kb_lds = smem + buf * 2 * G::kTileB;
-    const char* vb_lds = kb_lds + G::kTileB;
-
-    // ---- S^T = K Q^T for 64 keys x 32*QB queries.
-    f32x16 s[kKB][QB];
-#pragma unroll
-    for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][qb][r] = 0.f;
-#pragma unroll
-    for (int cc = 0; cc < G::kDC; ++cc) {
-#pragma unroll
-      for (int kb = 0; kb < kKB; ++kb) {
-        const int r = kb * 32 + col;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb_lds + r * G::kRowB + G::swz_k(r, 2 * cc + hf) * 16);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][cc], s[kb][qb], 0, 0, 0);
-      }
-    }
-
-    // ---- keys past the end of the sequence (last tile only) get -inf.
-    const int kv0 = t * kBN;
-    if (kv0 + kBN > skv) {
-#pragma unroll
-      for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          if (key >= skv)
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) s[kb][qb][r] = -INFINITY;
-        }
-    }
-
-    // ---- online softmax (base 2) per query column; P in bf16 as MFMA B operand.
-    u32x4 pb[kKB][QB][2];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
-      mx = fmaxf(mx, other_half(mx));
-      const float m_new = fmaxf(m_run[qb], mx * c);
-      const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
-      m_run[qb] = m_new;
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < kKB; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][r], c, -m_new));
-          s[kb][qb][r] = p;
-          rs += p;
-        }
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            pb[kb][qb][u][e] = pack_bf16x2(s[kb][qb][8 * u + 2 * e], s[kb][qb][8 * u + 2 * e + 1]);
-      }
-      l_run[qb] = l_run[qb] * alpha + rs;
-#pragma unroll
-      for (int db = 0; db < G::kND; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc_o[db][qb][r] *= alpha;
-    }
-
-    // ---- O^T += V^T P^T.  MFMA (kb, u) contracts keys kb*32 + 16u + {4hf..4hf+3, 8+4hf..8+4hf+3}
-    // in k-slots 8hf..8hf+7, the order in which the S^T accumulator holds them.
-    const int g16 = lane >> 4, j16 = lane & 15;
-#pragma unroll
-    for (int kb = 0; kb < kKB; ++kb) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int r0 = kb * 32 + 16 * u + 4 * hf + (j16 >> 2);
-#pragma unroll
-        for (int db = 0; db < G::kND; ++db) {
-          const int dcol = db * 32 + 16 * (g16 & 1) + 4 * (j16 & 3);
-          const int ch = dcol >> 3, inb = (dcol & 7) * 2;
-          const lds_i16x4* p0 = (const lds_i16x4*)(vb_lds + r0 * G::kRowB + G::swz_v(r0, ch) * 16 + inb);
-          const lds_i16x4* p1 = (const lds_i16x4*)(vb_lds + (r0 + 8) * G::kRowB + G::swz_v(r0 + 8, ch) * 16 + inb);
-          const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_i16x4*>(p0));
-          const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_i16x4*>(p1));
-          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            acc_o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                a, __builtin_bit_cast(bf16x8, pb[kb][qb][u]), acc_o[db][qb], 0, 0, 0);
-        }
-      }
-    }
-
-    if (more) stage_store(buf ^ 1);
-    __syncthreads();
-  }
-
-  // ---- epilogue: O = O^T / l, rows past sq are dropped.
+  // Epilogue: O = O^T / l, rows past sq are dropped.
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const float lt = l_run[qb] + other_half(l_run[qb]);
+    const float lt = halves_sum(st.l_run[qb]);
     const float inv = 1.f / lt;
     const int row = qrow0 + qb * 32 + col;
     if (row < sq) {
@@ -276,28 +474,25 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(
         for (int g = 0; g < 4; ++g) {
           const int d0 = db * 32 + 8 * g + 4 * hf;
           u32x2 w;
-          w[0] = pack_bf16x2(acc_o[db][qb][4 * g] * inv, acc_o[db][qb][4 * g + 1] * inv);
-          w[1] = pack_bf16x2(acc_o[db][qb][4 * g + 2] * inv, acc_o[db][qb][4 * g + 3] * inv);
+          w[0] = pack_bf16x2(acc[db][qb][4 * g] * inv, acc[db][qb][4 * g + 1] * inv);
+          w[1] = pack_bf16x2(acc[db][qb][4 * g + 2] * inv, acc[db][qb][4 * g + 3] * inv);
           *reinterpret_cast<u32x2*>(dst + d0) = w;
         }
-      if (lse && hf == 0) lse[int64_t(h) * sq + row] = (m_run[qb] + __log2f(lt)) * kLn2;
+      if (lse && hf == 0) lse[int64_t(h) * sq + row] = (st.m_run[qb] + __log2f(lt)) * kLn2;
     }
   }
 }
 
-template <int D, int QB>
-hipError_t launch_cfg(const void* q, const void* k, const void* v, void* o, float* lse, int64_t sq,
-                      int64_t skv, int H, float c, hipStream_t stream) {
-  constexpr int BM = kWaves * 32 * QB;
+template <int D>
+hipError_t launch_d(const void* q, const void* k, const void* v, void* o, float* lse, int64_t sq, int64_t skv,
+                    int H, float c, hipStream_t stream) {
   const int64_t nqt = (sq + BM - 1) / BM;
-  const int64_t nwg = nqt * H;
-  const int64_t per = (nwg + 7) / 8;
-  const int64_t grid = per * 8;
+  const int64_t grid = nqt * H;
   if (grid > kMaxGrid) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((attn_bf16_kernel<D, QB>), dim3(unsigned(grid)), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((attn_bf16_kernel<D>), dim3(unsigned(grid)), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, int(sq), int(skv), H,
-                     c, int(nqt), int(nwg), int(per));
+                     static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, int(sq), int(skv), H, c,
+                     int(nqt));
   return hipGetLastError();
 }
 
@@ -307,8 +502,8 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o
                             int64_t skv, int H, int d, float scale, hipStream_t stream) {
   if (sq > (int64_t(1) << 31) - 1024) return hipErrorInvalidValue;
   const float c = scale * 1.4426950408889634f;
-  if (d == 64) return launch_cfg<64, 1>(q, k, v, o, lse, sq, skv, H, c, stream);
-  return launch_cfg<128, 1>(q, k, v, o, lse, sq, skv, H, c, stream);
+  if (d == 64) return launch_d<64>(q, k, v, o, lse, sq, skv, H, c, stream);
+  return launch_d<128>(q, k, v, o, lse, sq, skv, H, c, stream);
 }
 
 }  // namespace spattn

@@ -233,6 +233,9 @@ int shard_attn_fwd(int32_t dtype, const void* q, const void* k, const void* v, v
   if ((sq + 31) / 32 > spattn::kMaxGrid / H)
     return fail(SP_ERANGE, "shard_attn_fwd: sq*H too large for one launch");
   if (skv > (int64_t(1) << 31) - 256) return fail(SP_ERANGE, "shard_attn_fwd: skv must be < 2^31");
+  // The kernels address a 64-token K/V tile with 32-bit byte offsets.
+  if (int64_t(H) * d * 4 * 64 > (int64_t(1) << 31) - 1)
+    return fail(SP_ERANGE, "shard_attn_fwd: H*d too large (64 tokens of K must span < 2 GiB)");
   if (sq == 0) return ok();
   if (!q || !k || !v || !o) return fail(SP_EINVAL, "shard_attn_fwd: null device pointer");
   if (ranges_overlap(o, qb, q, qb) || ranges_overlap(o, qb, k, kb) || ranges_overlap(o, qb, v, kb))
