@@ -282,57 +282,135 @@ __device__ inline void pv32(f32x16 (&o)[Geo<D>::kND][QB], const PW& pb, const ch
   }
 }
 
-// Instruction-group masks of __builtin_amdgcn_sched_group_barrier.
-// (VALU excludes transcendental instructions, which have their own mask.)
-constexpr int kSgVALU = 0x002, kSgMFMA = 0x008, kSgDSRead = 0x100, kSgTrans = 0x400;
-
-// One 32-key step.  On entry `cur` holds S^T of the step's keys and `st` its
-// reference maximum (block_max already applied).  Region A: the MFMAs compute
-// S^T of the next 32 keys into `nxt` while the VALU turns `cur` into bf16
-// probabilities.  Region B: the MFMAs accumulate P*V while the VALU adds the
-// row sums and takes the maximum of `nxt`.  Both regions are branch-free so
-// the scheduler can interleave MFMA and VALU work as the groups below ask.
+// One 32-key step, issued in a fixed order: every MFMA is followed by its
+// share of the VALU work and a scheduling fence, so the SIMD's in-order issue
+// alternates matrix and vector instructions (an MFMA occupies the matrix pipe
+// for 8 passes while the following VALU instructions issue), and LDS operand
+// reads are issued two MFMA pairs ahead of their use.
+//
+// On entry `cur` holds S^T of the step's keys and `st` its reference maximum.
+// Part A: MFMAs compute S^T of the next 32 keys into `nxt` (HAS_NEXT) while the
+//         VALU turns `cur` into bf16 probabilities (fma, exp2, cvt).
+// Part B: MFMAs accumulate P*V while the VALU adds the row sums (v_dot2) and
+//         takes the maximum of `nxt`.
 template <int D, bool HAS_NEXT, bool MASK_NEXT>
 __device__ inline void step32(f32x16 (&cur)[QB], f32x16 (&nxt)[QB], SoftState& st, PW& pb,
                               f32x16 (&acc)[Geo<D>::kND][QB], const bf16x8 (&qf)[QB][Geo<D>::kDC],
                               const char* kb_next, int rk_next, const f32x16& init_next, const char* vb, int rv,
                               float c, int lane, int col, int hf) {
   using G = Geo<D>;
+  constexpr int kA = 2 * G::kDC;      // MFMAs of part A (S^T of the next block)
+  constexpr int kPA = 16 / kA;        // probability pairs per part-A slot (32 values per lane)
+  constexpr int kB = 4 * G::kND;      // MFMAs of part B (P*V)
   if (st.any) rescale_o<D>(acc, st.alpha);
   __builtin_amdgcn_sched_barrier(0);
-  // region A: 16 MFMAs (with the 8 K-fragment reads two groups ahead) and the
-  // 32 exponentials + 48 other VALU instructions of the probabilities.
-  if (HAS_NEXT) qk32<D, MASK_NEXT>(nxt, kb_next, rk_next, qf, init_next, col, hf);
-  probs(cur, pb, st, c);
-  if (HAS_NEXT) {
-    __builtin_amdgcn_sched_group_barrier(kSgDSRead, 2, 0);
+
+  // ---- part A
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float ls[QB];
 #pragma unroll
-    for (int i = 0; i < G::kDC; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSgMFMA, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSgVALU, 3, 0);
-      __builtin_amdgcn_sched_group_barrier(kSgTrans, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(kSgMFMA, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSgVALU, 3, 0);
-      __builtin_amdgcn_sched_group_barrier(kSgTrans, 2, 0);
-      if (i + 2 < G::kDC) __builtin_amdgcn_sched_group_barrier(kSgDSRead, 1, 0);
+  for (int qb = 0; qb < QB; ++qb) ls[qb] = st.l_run[qb] * st.alpha[qb];
+  const int rk = rk_next + col;
+  const char* krow = kb_next + rk * G::kRowB;
+  const int ksw = G::swz_k(rk);
+  auto kread = [&](int cc) {
+    return *reinterpret_cast<const bf16x8*>(krow + (((2 * cc + hf) ^ ksw) << 4));
+  };
+  bf16x8 kf[G::kDC];
+  if (HAS_NEXT) {
+    kf[0] = kread(0);
+    kf[1] = kread(1);
+  }
+#pragma unroll
+  for (int i = 0; i < kA; ++i) {
+    const int cc = i >> 1, qb = i & 1;
+    if (HAS_NEXT) {
+      if (qb == 0 && cc + 2 < G::kDC) kf[cc + 2] = kread(cc + 2);
+      if (cc > 0)
+        nxt[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cc], qf[qb][cc], nxt[qb], 0, 0, 0);
+      else if (MASK_NEXT)
+        nxt[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cc], qf[qb][cc], init_next, 0, 0, 0);
+      else
+        nxt[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cc], qf[qb][cc], f32x16{}, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < kPA; ++j) {
+      const int w = i * kPA + j;          // pair index 0..15
+      const int pq = w >> 3, pr = w & 7;  // query block, pair within the block
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(cur[pq][2 * pr], c, -st.m_run[pq]));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(cur[pq][2 * pr + 1], c, -st.m_run[pq]));
+      const uint32_t word = pack_bf16x2(p0, p1);
+      pb[pq][pr >> 2][pr & 3] = word;
+      ls[pq] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, word), ones, ls[pq], false);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // Keep the row sums in part A: an empty asm consuming them stops IR passes
+  // from sinking the v_dot2 chain past the fences into the next step.
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    asm volatile("" : "+v"(ls[qb]));
+    st.l_run[qb] = ls[qb];
+  }
+
+  // ---- part B
+  const int g16 = lane >> 4, j16 = lane & 15;
+  auto vread = [&](int k) {  // V^T fragment of MFMA pair k = u * kND + db
+    const int u = k / G::kND, db = k % G::kND;
+    const int ra = rv + 16 * u + 4 * hf + (j16 >> 2);
+    const int dcol = db * 32 + 16 * (g16 & 1) + 4 * (j16 & 3);
+    const int ch = dcol >> 3, inb = (dcol & 7) * 2;
+    const char* p0 = vb + ra * G::kRowB + ((ch ^ G::swz_v(ra)) << 4) + inb;
+    const char* p1 = vb + (ra + 8) * G::kRowB + ((ch ^ G::swz_v(ra + 8)) << 4) + inb;
+    const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
+    const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p1);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  float mx[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) mx[qb] = -INFINITY;
+  bf16x8 vf[2 * G::kND];
+  vf[0] = vread(0);
+  vf[1] = vread(1);
+#pragma unroll
+  for (int i = 0; i < kB; ++i) {
+    const int k = i >> 1, qb = i & 1;  // MFMA pair k (one V fragment), query block qb
+    const int u = k / G::kND, db = k % G::kND;
+    if (qb == 0 && k + 2 < 2 * G::kND) vf[k + 2] = vread(k + 2);
+    acc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+        vf[k], __builtin_bit_cast(bf16x8, u32x4{pb[qb][u][0], pb[qb][u][1], pb[qb][u][2], pb[qb][u][3]}),
+        acc[db][qb], 0, 0, 0);
+    // maxima of the next block, spread over the slots
+    if (HAS_NEXT) {
+      constexpr int per = (QB * 8) / kB;  // v_max3 work items per slot
+#pragma unroll
+      for (int j = 0; j < (per > 0 ? per : 1); ++j) {
+        const int x = per > 0 ? i * per + j : i;
+        if (x < QB * 8 && (per > 0 || (i % (kB / (QB * 8))) == 0)) {
+          const int xx = per > 0 ? x : i / (kB / (QB * 8));
+          const int xq = xx >> 3, xr = xx & 7;
+          mx[xq] = fmaxf(mx[xq], fmaxf(nxt[xq][2 * xr], nxt[xq][2 * xr + 1]));
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (HAS_NEXT) {
+    float mt[QB];
+    bool need = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      mt[qb] = other_half_max(mx[qb]) * c;
+      need |= mt[qb] > st.m_run[qb] + kTau;
+    }
+    st.any = __builtin_amdgcn_ballot_w64(need) != 0;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float m_new = st.any ? fmaxf(st.m_run[qb], mt[qb]) : st.m_run[qb];
+      st.alpha[qb] = __builtin_amdgcn_exp2f(st.m_run[qb] - m_new);
+      st.m_run[qb] = m_new;
     }
   }
-  __builtin_amdgcn_sched_barrier(0);
-  // region B: 16 MFMAs (V^T fragments read two pairs ahead), row sums and the
-  // maximum of the next block.
-  pv32<D>(acc, pb, vb, rv, lane, hf);
-  row_sums(pb, st);
-  if (HAS_NEXT) block_max(nxt, st, c);
-  __builtin_amdgcn_sched_group_barrier(kSgDSRead, 4, 1);
-#pragma unroll
-  for (int i = 0; i < 2 * G::kND; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kSgMFMA, 1, 1);
-    __builtin_amdgcn_sched_group_barrier(kSgVALU, 2, 1);
-    __builtin_amdgcn_sched_group_barrier(kSgMFMA, 1, 1);
-    __builtin_amdgcn_sched_group_barrier(kSgVALU, 2, 1);
-    if (i + 2 < 2 * G::kND) __builtin_amdgcn_sched_group_barrier(kSgDSRead, 2, 1);
-  }
-  __builtin_amdgcn_sched_barrier(0);
 }
 
 __device__ inline void wait_loads_and_barrier() {
