@@ -52,13 +52,26 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kWaves = 4;
+#ifndef SPATTN_WAVES
+#define SPATTN_WAVES 4
+#endif
+#ifndef SPATTN_QB
+#define SPATTN_QB 2
+#endif
+constexpr int kWaves = SPATTN_WAVES;   // waves per work-group
 constexpr int kThreads = 64 * kWaves;
-constexpr int QB = 2;                  // 32-query MFMA blocks per wave
+constexpr int QB = SPATTN_QB;          // 32-query MFMA blocks per wave
 constexpr int BM = kWaves * 32 * QB;   // query rows per work-group
+#ifndef SPATTN_LEAD
+#define SPATTN_LEAD 2
+#endif
+constexpr int kLead = SPATTN_LEAD;     // K/V tiles in flight ahead of the tile being used
+constexpr int kKSlots = kLead + 2;     // LDS slots for K: tiles t, t+1 read, t+2 .. t+1+kLead loading
+constexpr int kVSlots = kLead + 1;     // LDS slots for V: tile t read, t+1 .. t+kLead loading
 constexpr int kBN = 64;                // keys per tile
 constexpr int kKB = kBN / 32;          // 32-key blocks per tile
 constexpr float kTau = 8.0f;           // lazy-rescale threshold (log2 units)
@@ -117,30 +130,42 @@ struct TileLoader {
       voff[i] = uint32_t(r * rowbytes + c * 16);
     }
   }
+  // Buffer resource of a 64-row tile: base address, stride 0 (raw), 2 GiB range.
+  static __device__ i32x4 rsrc(const char* base) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    return i32x4{int(uint32_t(a)), int(uint32_t(a >> 32) & 0xFFFF), 0x7FFFFFFF, 0x00020000};
+  }
+  // One LDS-direct 16-byte load per lane.  Issued as inline asm so that the
+  // compiler does not treat these in-flight LDS writes as aliasing every LDS
+  // read that follows (it would wait for them with vmcnt(0) before the first
+  // transposing read and serialise the tile pipeline).  The kernel waits for
+  // them itself, with vmcnt, before the barrier that publishes a tile.
+  static __device__ void issue(const i32x4& rs, char* lds_blk, uint32_t voffset) {
+    // LDS address of this wave's 1 KiB block (wave-uniform; M0 needs an SGPR)
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>(lds_blk)));
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(m0), "v"(voffset), "s"(rs)
+                 : "memory", "m0");
+  }
   // Full tile: every row < skv.
   __device__ void load(const uint16_t* hb, int tile, int64_t rowbytes, char* lds, int wave) const {
     const char* base = reinterpret_cast<const char*>(hb) + int64_t(tile) * kBN * rowbytes;
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, 0x7FFFFFFF, 0x00020000);
+    const i32x4 rs = rsrc(base);
 #pragma unroll
-    for (int i = 0; i < G::kLoads; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + (wave * G::kLoads + i) * 1024), 16, voff[i],
-                                               0, 0, 0);
+    for (int i = 0; i < G::kLoads; ++i) issue(rs, lds + (wave * G::kLoads + i) * 1024, voff[i]);
   }
   // Last tile of a ragged sequence: rows >= skv re-read row skv-1 (finite data;
   // those keys are masked to -inf, so they carry zero weight).
   __device__ void load_clamped(const uint16_t* hb, int tile, int skv, int64_t rowbytes, char* lds,
                                int wave) const {
     const char* base = reinterpret_cast<const char*>(hb) + int64_t(tile) * kBN * rowbytes;
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, 0x7FFFFFFF, 0x00020000);
+    const i32x4 rs = rsrc(base);
     const int valid = skv - tile * kBN;
 #pragma unroll
     for (int i = 0; i < G::kLoads; ++i) {
       const int over = rows[i] >= valid ? rows[i] - (valid - 1) : 0;
-      const uint32_t off = voff[i] - uint32_t(over * rowbytes);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + (wave * G::kLoads + i) * 1024), 16, off, 0,
-                                               0, 0);
+      issue(rs, lds + (wave * G::kLoads + i) * 1024, voff[i] - uint32_t(over * rowbytes));
     }
   }
 };
@@ -293,67 +318,37 @@ __device__ inline void pv32(f32x16 (&o)[Geo<D>::kND][QB], const PW& pb, const ch
 //         VALU turns `cur` into bf16 probabilities (fma, exp2, cvt).
 // Part B: MFMAs accumulate P*V while the VALU adds the row sums (v_dot2) and
 //         takes the maximum of `nxt`.
-template <int D, bool HAS_NEXT, bool MASK_NEXT>
+template <int D>
+__device__ inline bf16x8 k_frag(const char* kb, int r0, int cc, int col, int hf) {
+  using G = Geo<D>;
+  const int r = r0 + col;
+  return *reinterpret_cast<const bf16x8*>(kb + r * G::kRowB + (((2 * cc + hf) ^ G::swz_k(r)) << 4));
+}
+
+// Work items spread evenly over the issue slots of a part: slot i of M runs
+// items [i*N/M, (i+1)*N/M) of N.
+template <int N, int M, typename F>
+__device__ inline void slot_items(int i, F&& f) {
+#pragma unroll
+  for (int w = 0; w < N; ++w)
+    if (w * M / N == i) f(w);
+}
+
+template <int D, bool HAS_NEXT, bool MASK_NEXT, bool PRE_NEXT>
 __device__ inline void step32(f32x16 (&cur)[QB], f32x16 (&nxt)[QB], SoftState& st, PW& pb,
                               f32x16 (&acc)[Geo<D>::kND][QB], const bf16x8 (&qf)[QB][Geo<D>::kDC],
                               const char* kb_next, int rk_next, const f32x16& init_next, const char* vb, int rv,
-                              float c, int lane, int col, int hf) {
+                              float c, int lane, int col, int hf, bf16x8 (&kpre)[2], const char* kb_after,
+                              int rk_after) {
   using G = Geo<D>;
-  constexpr int kA = 2 * G::kDC;      // MFMAs of part A (S^T of the next block)
-  constexpr int kPA = 16 / kA;        // probability pairs per part-A slot (32 values per lane)
-  constexpr int kB = 4 * G::kND;      // MFMAs of part B (P*V)
+  constexpr int kA = QB * G::kDC;      // MFMA slots of part A: S^T of the next block
+  constexpr int kB = 2 * QB * G::kND;  // MFMA slots of part B: P*V
+  constexpr int kNV = 2 * G::kND;      // V^T fragments (MFMA pairs u, db) per step
+  static_assert(kA >= 4 && kB >= 4, "prefetch slots");
   if (st.any) rescale_o<D>(acc, st.alpha);
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- part A
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  float ls[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) ls[qb] = st.l_run[qb] * st.alpha[qb];
-  const int rk = rk_next + col;
-  const char* krow = kb_next + rk * G::kRowB;
-  const int ksw = G::swz_k(rk);
-  auto kread = [&](int cc) {
-    return *reinterpret_cast<const bf16x8*>(krow + (((2 * cc + hf) ^ ksw) << 4));
-  };
-  bf16x8 kf[G::kDC];
-  if (HAS_NEXT) {
-    kf[0] = kread(0);
-    kf[1] = kread(1);
-  }
-#pragma unroll
-  for (int i = 0; i < kA; ++i) {
-    const int cc = i >> 1, qb = i & 1;
-    if (HAS_NEXT) {
-      if (qb == 0 && cc + 2 < G::kDC) kf[cc + 2] = kread(cc + 2);
-      if (cc > 0)
-        nxt[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cc], qf[qb][cc], nxt[qb], 0, 0, 0);
-      else if (MASK_NEXT)
-        nxt[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cc], qf[qb][cc], init_next, 0, 0, 0);
-      else
-        nxt[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cc], qf[qb][cc], f32x16{}, 0, 0, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < kPA; ++j) {
-      const int w = i * kPA + j;          // pair index 0..15
-      const int pq = w >> 3, pr = w & 7;  // query block, pair within the block
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(cur[pq][2 * pr], c, -st.m_run[pq]));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(cur[pq][2 * pr + 1], c, -st.m_run[pq]));
-      const uint32_t word = pack_bf16x2(p0, p1);
-      pb[pq][pr >> 2][pr & 3] = word;
-      ls[pq] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, word), ones, ls[pq], false);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  // Keep the row sums in part A: an empty asm consuming them stops IR passes
-  // from sinking the v_dot2 chain past the fences into the next step.
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    asm volatile("" : "+v"(ls[qb]));
-    st.l_run[qb] = ls[qb];
-  }
-
-  // ---- part B
+  // V^T fragment reads (issued from the end of part A on)
   const int g16 = lane >> 4, j16 = lane & 15;
   auto vread = [&](int k) {  // V^T fragment of MFMA pair k = u * kND + db
     const int u = k / G::kND, db = k % G::kND;
@@ -369,30 +364,74 @@ __device__ inline void step32(f32x16 (&cur)[QB], f32x16 (&nxt)[QB], SoftState& s
   float mx[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) mx[qb] = -INFINITY;
-  bf16x8 vf[2 * G::kND];
-  vf[0] = vread(0);
-  vf[1] = vread(1);
+  bf16x8 vf[kNV];
+
+  // ---- part A: MFMA slot i computes (cc = i / QB, qb = i % QB) of S^T(next);
+  // the VALU produces the bf16 probability words of `cur` and their row sums.
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float ls[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) ls[qb] = st.l_run[qb] * st.alpha[qb];
+  const int rk = rk_next + col;
+  const char* krow = kb_next + rk * G::kRowB;
+  const int ksw = G::swz_k(rk);
+  auto kread = [&](int cc) {
+    return *reinterpret_cast<const bf16x8*>(krow + (((2 * cc + hf) ^ ksw) << 4));
+  };
+  bf16x8 kf[G::kDC];
+  if (HAS_NEXT) {
+    kf[0] = kpre[0];
+    kf[1] = kpre[1];
+  }
+#pragma unroll
+  for (int i = 0; i < kA; ++i) {
+    const int cc = i / QB, qb = i % QB;
+    if (HAS_NEXT) {
+      if (qb == 0 && cc + 2 < G::kDC) kf[cc + 2] = kread(cc + 2);
+      if (cc > 0)
+        nxt[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cc], qf[qb][cc], nxt[qb], 0, 0, 0);
+      else if (MASK_NEXT)
+        nxt[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cc], qf[qb][cc], init_next, 0, 0, 0);
+      else
+        nxt[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cc], qf[qb][cc], f32x16{}, 0, 0, 0);
+    }
+    slot_items<8 * QB, kA>(i, [&](int w) {  // word w: query block w/8, pair w%8
+      const int pq = w >> 3, pr = w & 7;
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(cur[pq][2 * pr], c, -st.m_run[pq]));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(cur[pq][2 * pr + 1], c, -st.m_run[pq]));
+      const uint32_t word = pack_bf16x2(p0, p1);
+      pb[pq][pr >> 2][pr & 3] = word;
+      ls[pq] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, word), ones, ls[pq], false);
+    });
+    if (i == kA - 4) vf[0] = vread(0);
+    if (i == kA - 3) vf[1] = vread(1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // Keep the row sums in part A: an empty asm consuming them stops IR passes
+  // from sinking the v_dot2 chain past the fences into the next step.
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    asm volatile("" : "+v"(ls[qb]));
+    st.l_run[qb] = ls[qb];
+  }
+
+  // ---- part B: MFMA slot i accumulates pair k = i / QB (u, db) for qb = i % QB;
+  // the VALU takes the maximum of the next block.
 #pragma unroll
   for (int i = 0; i < kB; ++i) {
-    const int k = i >> 1, qb = i & 1;  // MFMA pair k (one V fragment), query block qb
+    const int k = i / QB, qb = i % QB;
     const int u = k / G::kND, db = k % G::kND;
-    if (qb == 0 && k + 2 < 2 * G::kND) vf[k + 2] = vread(k + 2);
+    if (qb == 0 && k + 2 < kNV) vf[k + 2] = vread(k + 2);
     acc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
         vf[k], __builtin_bit_cast(bf16x8, u32x4{pb[qb][u][0], pb[qb][u][1], pb[qb][u][2], pb[qb][u][3]}),
         acc[db][qb], 0, 0, 0);
-    // maxima of the next block, spread over the slots
-    if (HAS_NEXT) {
-      constexpr int per = (QB * 8) / kB;  // v_max3 work items per slot
-#pragma unroll
-      for (int j = 0; j < (per > 0 ? per : 1); ++j) {
-        const int x = per > 0 ? i * per + j : i;
-        if (x < QB * 8 && (per > 0 || (i % (kB / (QB * 8))) == 0)) {
-          const int xx = per > 0 ? x : i / (kB / (QB * 8));
-          const int xq = xx >> 3, xr = xx & 7;
-          mx[xq] = fmaxf(mx[xq], fmaxf(nxt[xq][2 * xr], nxt[xq][2 * xr + 1]));
-        }
-      }
-    }
+    if (HAS_NEXT)
+      slot_items<8 * QB, kB>(i, [&](int w) {
+        const int xq = w >> 3, xr = w & 7;
+        mx[xq] = fmaxf(mx[xq], fmaxf(nxt[xq][2 * xr], nxt[xq][2 * xr + 1]));
+      });
+    if (PRE_NEXT && i == kB - 4) kpre[0] = k_frag<D>(kb_after, rk_after, 0, col, hf);
+    if (PRE_NEXT && i == kB - 3) kpre[1] = k_frag<D>(kb_after, rk_after, 1, col, hf);
     __builtin_amdgcn_sched_barrier(0);
   }
   if (HAS_NEXT) {
@@ -413,9 +452,20 @@ __device__ inline void step32(f32x16 (&cur)[QB], f32x16 (&nxt)[QB], SoftState& s
   }
 }
 
-__device__ inline void wait_loads_and_barrier() {
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's LDS-direct loads have landed
-  __syncthreads();
+// s_waitcnt immediate: vmcnt(vm), expcnt untouched, lgkmcnt(0).
+constexpr unsigned waitcnt_vm_lgkm0(unsigned vm) { return (vm & 0xFu) | ((vm >> 4) << 14) | (0x7u << 4); }
+
+// Tile barrier: this wave's older LDS-direct loads (all but the newest
+// PENDING) have landed and its LDS reads have completed, then all waves meet.
+// A bare s_barrier is used (the workgroup fences of __syncthreads would also
+// wait for the loads still meant to be in flight); the signal fences stop the
+// compiler from moving LDS accesses across it.
+template <unsigned PENDING>
+__device__ inline void tile_barrier() {
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(PENDING));
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 template <int D>
@@ -423,9 +473,10 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ lse, int sq, int skv, int H, float c, int nqt) {
   using G = Geo<D>;
-  // K tiles triple buffered (tile t is still read while tile t+2 streams in), V double.
-  __shared__ __attribute__((aligned(1024))) char smem[5 * G::kTileB];
-  char* const vbase = smem + 3 * G::kTileB;
+  // K tile j lives in slot j mod kKSlots, V tile j in slot j mod kVSlots.
+  __shared__ __attribute__((aligned(1024))) char smem[(kKSlots + kVSlots) * G::kTileB];
+  char* const vbase = smem + kKSlots * G::kTileB;
+  constexpr unsigned kBatch = 2 * G::kLoads;  // LDS-direct loads per wave per tile (K and V)
 
   // Head-major order: consecutive work-groups (spread over all XCDs) share a head.
   const int L = blockIdx.x;
@@ -448,21 +499,29 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(
   TileLoader<D, true> vl;
   kl.init(wave, lane, rowbytes);
   vl.init(wave, lane, rowbytes);
-  auto load_k = [&](int tile, int slot) {
-    char* dst = smem + slot * G::kTileB;
-    if (ragged && tile == nT - 1) kl.load_clamped(kh, tile, skv, rowbytes, dst, wave);
-    else kl.load(kh, tile, rowbytes, dst, wave);
+  auto kslot = [&](int j) { return smem + (j % kKSlots) * G::kTileB; };
+  auto vslot = [&](int j) { return vbase + (j % kVSlots) * G::kTileB; };
+  // Tile indices past the end are clamped: those loads land in slots no live
+  // tile uses and keep every batch the same size for the vmcnt accounting.
+  auto load_k = [&](int j) {
+    const int tile = min(j, nT - 1);
+    if (ragged && tile == nT - 1) kl.load_clamped(kh, tile, skv, rowbytes, kslot(j), wave);
+    else kl.load(kh, tile, rowbytes, kslot(j), wave);
   };
-  auto load_v = [&](int tile, int slot) {
-    char* dst = vbase + slot * G::kTileB;
-    if (ragged && tile == nT - 1) vl.load_clamped(vh, tile, skv, rowbytes, dst, wave);
-    else vl.load(vh, tile, rowbytes, dst, wave);
+  auto load_v = [&](int j) {
+    const int tile = min(j, nT - 1);
+    if (ragged && tile == nT - 1) vl.load_clamped(vh, tile, skv, rowbytes, vslot(j), wave);
+    else vl.load(vh, tile, rowbytes, vslot(j), wave);
+  };
+  // Batch j = {K tile j+1, V tile j}; tile t needs batch t.
+  auto load_batch = [&](int j) {
+    load_k(j + 1);
+    load_v(j);
   };
 
-  // K tiles 0 and 1 and V tile 0 start streaming while Q is loaded.
-  load_k(0, 0);
-  load_k(min(1, nT - 1), 1);
-  load_v(0, 0);
+  load_k(0);
+#pragma unroll
+  for (int j = 0; j < kLead; ++j) load_batch(j);
 
   // Q fragments (B operand of S^T = K Q^T): lane holds 8 d-values of one query.
   bf16x8 qf[QB][G::kDC];
@@ -497,46 +556,52 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(
   f32x16 sa[QB], sb[QB];  // S^T of the current / next 32 keys
   PW pb;
 
-  wait_loads_and_barrier();
-  if (nT == 1) qk32<D, true>(sa, smem, 0, qf, tail_init(0, skv, hf), col, hf);
-  else qk32<D, false>(sa, smem, 0, qf, zero, col, hf);
+  tile_barrier<0>();
+  if (nT == 1) qk32<D, true>(sa, kslot(0), 0, qf, tail_init(0, skv, hf), col, hf);
+  else qk32<D, false>(sa, kslot(0), 0, qf, zero, col, hf);
   block_max(sa, st, c);
+  // K fragments of the next step's part A are read ahead, at the end of the
+  // previous part B (that K tile has been resident since an earlier barrier).
+  bf16x8 kpre[2];
+  kpre[0] = k_frag<D>(kslot(0), 32, 0, col, hf);
+  kpre[1] = k_frag<D>(kslot(0), 32, 1, col, hf);
 
-  // Tile t (64 keys) = two 32-key steps.  Loads for K(t+2) and V(t+1) go to
-  // the buffers tile t-1 released (tile index clamped at the end).
-  int kcur = 0;  // LDS slot of K tile t (slots rotate mod 3)
-  auto tile_top = [&](int t) {
-    const int knext = kcur == 2 ? 0 : kcur + 1;
-    const int kfree = knext == 2 ? 0 : knext + 1;
-    wait_loads_and_barrier();
-    load_k(min(t + 2, nT - 1), kfree);
-    load_v(min(t + 1, nT - 1), (t + 1) & 1);
-    return knext;
-  };
+  // Tile t (64 keys) = two 32-key steps.  At its top batch t (K t+1, V t) has
+  // landed, batches t+1 .. t+kLead-1 may still be in flight, and batch
+  // t+kLead is issued into the slots tile t-1 released.
   int t = 0;
   for (; t < nT - 2; ++t) {  // the next tile is not the last one: no masking
-    const int knext = tile_top(t);
-    const char* vb = vbase + (t & 1) * G::kTileB;
-    step32<D, true, false>(sa, sb, st, pb, acc, qf, smem + kcur * G::kTileB, 32, zero, vb, 0, c, lane, col, hf);
-    step32<D, true, false>(sb, sa, st, pb, acc, qf, smem + knext * G::kTileB, 0, zero, vb, 32, c, lane, col, hf);
-    kcur = knext;
+    tile_barrier<kBatch * (kLead - 1)>();
+    load_batch(t + kLead);
+    const char* vb = vslot(t);
+    char* kbc = kslot(t);
+    char* kbn = kslot(t + 1);
+    step32<D, true, false, true>(sa, sb, st, pb, acc, qf, kbc, 32, zero, vb, 0, c, lane, col, hf, kpre, kbn, 0);
+    step32<D, true, false, true>(sb, sa, st, pb, acc, qf, kbn, 0, zero, vb, 32, c, lane, col, hf, kpre, kbn, 32);
   }
   if (t == nT - 2) {  // the next tile is the last one
-    const int knext = tile_top(t);
-    const char* vb = vbase + (t & 1) * G::kTileB;
-    step32<D, true, false>(sa, sb, st, pb, acc, qf, smem + kcur * G::kTileB, 32, zero, vb, 0, c, lane, col, hf);
-    step32<D, true, true>(sb, sa, st, pb, acc, qf, smem + knext * G::kTileB, 0, tail_init(last0, skv, hf), vb, 32,
-                          c, lane, col, hf);
-    kcur = knext;
+    tile_barrier<kBatch * (kLead - 1)>();
+    load_batch(t + kLead);
+    const char* vb = vslot(t);
+    char* kbc = kslot(t);
+    char* kbn = kslot(t + 1);
+    step32<D, true, false, true>(sa, sb, st, pb, acc, qf, kbc, 32, zero, vb, 0, c, lane, col, hf, kpre, kbn, 0);
+    step32<D, true, true, true>(sb, sa, st, pb, acc, qf, kbn, 0, tail_init(last0, skv, hf), vb, 32, c, lane, col,
+                                hf, kpre, kbn, 32);
     ++t;
   }
-  {  // last tile
-    wait_loads_and_barrier();
-    const char* vb = vbase + (t & 1) * G::kTileB;
-    step32<D, true, true>(sa, sb, st, pb, acc, qf, smem + kcur * G::kTileB, 32, tail_init(last0 + 32, skv, hf), vb,
-                          0, c, lane, col, hf);
-    step32<D, false, false>(sb, sa, st, pb, acc, qf, nullptr, 0, zero, vb, 32, c, lane, col, hf);
+  {  // last tile: no further loads are issued
+    tile_barrier<kBatch * (kLead - 1)>();
+    const char* vb = vslot(t);
+    char* kbc = kslot(t);
+    step32<D, true, true, false>(sa, sb, st, pb, acc, qf, kbc, 32, tail_init(last0 + 32, skv, hf), vb, 0, c, lane,
+                                 col, hf, kpre, nullptr, 0);
+    step32<D, false, false, false>(sb, sa, st, pb, acc, qf, nullptr, 0, zero, vb, 32, c, lane, col, hf, kpre,
+                                   nullptr, 0);
   }
+  // No LDS-direct load may still be landing once this work-group's LDS is
+  // handed to the next one.
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
 
   // Epilogue: O = O^T / l, rows past sq are dropped.
 #pragma unroll
