@@ -88,7 +88,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="p768_15s_w4")
-    ap.add_argument("--cpu-rows", type=int, default=48, help="query rows in the CPU-oracle sample (0: skip)")
+    ap.add_argument("--cpu-rows", type=int, default=192, help="query rows in the CPU-oracle sample (0: skip)")
     args = ap.parse_args()
 
     if args.gpus != 1:
