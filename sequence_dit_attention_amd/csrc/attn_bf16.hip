@@ -206,31 +206,55 @@ __device__ inline f32x16 tail_init(int key0, int skv, int hf) {
 // Softmax state of the wave's 64 query columns (both wave halves hold the same values).
 struct SoftState {
   float m_run[QB];  // reference maximum (log2 units) the probabilities are taken against
+  float thr[QB];    // raw-score threshold (m_run + kTau) / c above which the reference is raised
   float l_run[QB];  // this lane's partial sum of bf16 probabilities
   float alpha[QB];  // factor taking the accumulators from the previous to the current reference
-  bool any;         // some column's reference moved: O must be scaled by alpha
+  bool any;         // some column's reference moved: O and l must be scaled by alpha
 };
 
-// Maximum of a 32-key block; raises the reference maximum of every column of
-// the wave when any column's block maximum exceeds its reference by > kTau.
-__device__ inline void block_max(const f32x16 (&s)[QB], SoftState& st, float c) {
-  float mt[QB];
+// max(a, b, c) in one instruction (the compiler would otherwise build a
+// max/max/max3 tree).  Operands are finite floats or -inf.
+__device__ inline float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// Reference update after the block maxima mx (raw scores, per lane: the
+// lane's 16 keys of its query column) are known.  The common case is one
+// compare per query block and a ballot.  Only when some lane's maximum
+// exceeds its column's threshold are the two wave halves combined and the
+// columns whose maximum really exceeds the reference by more than kTau
+// raised; every other column keeps its reference (alpha = 1 exactly), so a
+// row's arithmetic never depends on the other rows of the wave.
+__device__ inline void update_ref(const float (&mx)[QB], SoftState& st, float c) {
   bool need = false;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    float mx = fmaxf(s[qb][0], s[qb][1]);
-#pragma unroll
-    for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[qb][r], s[qb][r + 1]));
-    mt[qb] = other_half_max(mx) * c;
-    need |= mt[qb] > st.m_run[qb] + kTau;
-  }
+  for (int qb = 0; qb < QB; ++qb) need |= mx[qb] > st.thr[qb];
   st.any = __builtin_amdgcn_ballot_w64(need) != 0;
+  if (st.any) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float mt = other_half_max(mx[qb]) * c;
+      const float m_new = mt > st.m_run[qb] + kTau ? mt : st.m_run[qb];
+      st.alpha[qb] = __builtin_amdgcn_exp2f(st.m_run[qb] - m_new);
+      st.m_run[qb] = m_new;
+      st.thr[qb] = (m_new + kTau) * __builtin_amdgcn_rcpf(c);
+    }
+  }
+}
+
+// Maximum of a 32-key block, then the reference update.
+__device__ inline void block_max(const f32x16 (&s)[QB], SoftState& st, float c) {
+  float mx[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const float m_new = st.any ? fmaxf(st.m_run[qb], mt[qb]) : st.m_run[qb];
-    st.alpha[qb] = __builtin_amdgcn_exp2f(st.m_run[qb] - m_new);
-    st.m_run[qb] = m_new;
+    float m = fmaxf(s[qb][0], s[qb][1]);
+#pragma unroll
+    for (int r = 2; r < 16; r += 2) m = max3(m, s[qb][r], s[qb][r + 1]);
+    mx[qb] = m;
   }
+  update_ref(mx, st, c);
 }
 
 // Probabilities of a 32-key block as packed bf16 pairs: pw[qb][u][e] holds
@@ -238,35 +262,6 @@ __device__ inline void block_max(const f32x16 (&s)[QB], SoftState& st, float c) 
 // is the B operand of P*V MFMA u.  (Kept as plain 32-bit words: element
 // extraction from a vector type under __builtin_bit_cast was miscompiled.)
 typedef uint32_t PW[QB][2][4];
-
-// p = 2^(s*c - m) rounded to bf16 pairs: the B operands of P*V.
-__device__ inline void probs(const f32x16 (&s)[QB], PW& pb, const SoftState& st, float c) {
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[qb][8 * u + 2 * e], c, -st.m_run[qb]));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[qb][8 * u + 2 * e + 1], c, -st.m_run[qb]));
-        pb[qb][u][e] = pack_bf16x2(p0, p1);
-      }
-}
-
-// l = l * alpha + sum of the bf16 probabilities (v_dot2 against ones).
-__device__ inline void row_sums(const PW& pb, SoftState& st) {
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    float ls = st.l_run[qb] * st.alpha[qb];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pb[qb][u][e]), ones, ls, false);
-    st.l_run[qb] = ls;
-  }
-}
 
 template <int D>
 __device__ inline void rescale_o(f32x16 (&o)[Geo<D>::kND][QB], const float (&alpha)[QB]) {
@@ -345,7 +340,11 @@ __device__ inline void step32(f32x16 (&cur)[QB], f32x16 (&nxt)[QB], SoftState& s
   constexpr int kB = 2 * QB * G::kND;  // MFMA slots of part B: P*V
   constexpr int kNV = 2 * G::kND;      // V^T fragments (MFMA pairs u, db) per step
   static_assert(kA >= 4 && kB >= 4, "prefetch slots");
-  if (st.any) rescale_o<D>(acc, st.alpha);
+  if (st.any) {  // reference raised at the end of the previous step
+    rescale_o<D>(acc, st.alpha);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) st.l_run[qb] *= st.alpha[qb];
+  }
   __builtin_amdgcn_sched_barrier(0);
 
   // V^T fragment reads (issued from the end of part A on)
@@ -371,7 +370,7 @@ __device__ inline void step32(f32x16 (&cur)[QB], f32x16 (&nxt)[QB], SoftState& s
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   float ls[QB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) ls[qb] = st.l_run[qb] * st.alpha[qb];
+  for (int qb = 0; qb < QB; ++qb) ls[qb] = st.l_run[qb];
   const int rk = rk_next + col;
   const char* krow = kb_next + rk * G::kRowB;
   const int ksw = G::swz_k(rk);
@@ -428,28 +427,13 @@ __device__ inline void step32(f32x16 (&cur)[QB], f32x16 (&nxt)[QB], SoftState& s
     if (HAS_NEXT)
       slot_items<8 * QB, kB>(i, [&](int w) {
         const int xq = w >> 3, xr = w & 7;
-        mx[xq] = fmaxf(mx[xq], fmaxf(nxt[xq][2 * xr], nxt[xq][2 * xr + 1]));
+        mx[xq] = max3(mx[xq], nxt[xq][2 * xr], nxt[xq][2 * xr + 1]);
       });
     if (PRE_NEXT && i == kB - 4) kpre[0] = k_frag<D>(kb_after, rk_after, 0, col, hf);
     if (PRE_NEXT && i == kB - 3) kpre[1] = k_frag<D>(kb_after, rk_after, 1, col, hf);
     __builtin_amdgcn_sched_barrier(0);
   }
-  if (HAS_NEXT) {
-    float mt[QB];
-    bool need = false;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      mt[qb] = other_half_max(mx[qb]) * c;
-      need |= mt[qb] > st.m_run[qb] + kTau;
-    }
-    st.any = __builtin_amdgcn_ballot_w64(need) != 0;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float m_new = st.any ? fmaxf(st.m_run[qb], mt[qb]) : st.m_run[qb];
-      st.alpha[qb] = __builtin_amdgcn_exp2f(st.m_run[qb] - m_new);
-      st.m_run[qb] = m_new;
-    }
-  }
+  if (HAS_NEXT) update_ref(mx, st, c);
 }
 
 // s_waitcnt immediate: vmcnt(vm), expcnt untouched, lgkmcnt(0).
@@ -548,7 +532,9 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     st.m_run[qb] = -INFINITY;
+    st.thr[qb] = -INFINITY;
     st.l_run[qb] = 0.f;
+    st.alpha[qb] = 1.f;
   }
   const f32x16 zero = {};
   const int last0 = (nT - 1) * kBN;  // first key of the last tile
