@@ -66,12 +66,18 @@ constexpr int kWaves = SPATTN_WAVES;   // waves per work-group
 constexpr int kThreads = 64 * kWaves;
 constexpr int QB = SPATTN_QB;          // 32-query MFMA blocks per wave
 constexpr int BM = kWaves * 32 * QB;   // query rows per work-group
+#ifndef SPATTN_RA
+#define SPATTN_RA 2  // LDS operand reads are issued this many MFMA groups ahead of their use
+#endif
+constexpr int kRA = SPATTN_RA;
 #ifndef SPATTN_LEAD
 #define SPATTN_LEAD 2
 #endif
 constexpr int kLead = SPATTN_LEAD;     // K/V tiles in flight ahead of the tile being used
-constexpr int kKSlots = kLead + 2;     // LDS slots for K: tiles t, t+1 read, t+2 .. t+1+kLead loading
-constexpr int kVSlots = kLead + 1;     // LDS slots for V: tile t read, t+1 .. t+kLead loading
+constexpr int pow2_ceil(int x) { return x <= 1 ? 1 : 2 * pow2_ceil((x + 1) / 2); }
+// Slot counts are rounded up to powers of two so that slot indices are masks.
+constexpr int kKSlots = pow2_ceil(kLead + 2);  // K: tiles t, t+1 read, t+2 .. t+1+kLead loading
+constexpr int kVSlots = pow2_ceil(kLead + 1);  // V: tile t read, t+1 .. t+kLead loading
 constexpr int kBN = 64;                // keys per tile
 constexpr int kKB = kBN / 32;          // 32-key blocks per tile
 constexpr float kTau = 8.0f;           // lazy-rescale threshold (log2 units)
@@ -152,6 +158,12 @@ struct TileLoader {
   __device__ void load(const uint16_t* hb, int tile, int64_t rowbytes, char* lds, int wave) const {
     const char* base = reinterpret_cast<const char*>(hb) + int64_t(tile) * kBN * rowbytes;
     const i32x4 rs = rsrc(base);
+#pragma unroll
+    for (int i = 0; i < G::kLoads; ++i) issue(rs, lds + (wave * G::kLoads + i) * 1024, voff[i]);
+  }
+  // Full tile at byte address `addr` (wave-uniform).
+  __device__ void load_at(uint64_t addr, char* lds, int wave) const {
+    const i32x4 rs = rsrc(reinterpret_cast<const char*>(addr));
 #pragma unroll
     for (int i = 0; i < G::kLoads; ++i) issue(rs, lds + (wave * G::kLoads + i) * 1024, voff[i]);
   }
@@ -333,13 +345,13 @@ template <int D, bool HAS_NEXT, bool MASK_NEXT, bool PRE_NEXT>
 __device__ inline void step32(f32x16 (&cur)[QB], f32x16 (&nxt)[QB], SoftState& st, PW& pb,
                               f32x16 (&acc)[Geo<D>::kND][QB], const bf16x8 (&qf)[QB][Geo<D>::kDC],
                               const char* kb_next, int rk_next, const f32x16& init_next, const char* vb, int rv,
-                              float c, int lane, int col, int hf, bf16x8 (&kpre)[2], const char* kb_after,
+                              float c, int lane, int col, int hf, bf16x8 (&kpre)[kRA], const char* kb_after,
                               int rk_after) {
   using G = Geo<D>;
   constexpr int kA = QB * G::kDC;      // MFMA slots of part A: S^T of the next block
   constexpr int kB = 2 * QB * G::kND;  // MFMA slots of part B: P*V
   constexpr int kNV = 2 * G::kND;      // V^T fragments (MFMA pairs u, db) per step
-  static_assert(kA >= 4 && kB >= 4, "prefetch slots");
+  static_assert(kA >= 2 * kRA && kB >= 2 * kRA, "prefetch slots");
   if (st.any) {  // reference raised at the end of the previous step
     rescale_o<D>(acc, st.alpha);
 #pragma unroll
@@ -379,14 +391,14 @@ __device__ inline void step32(f32x16 (&cur)[QB], f32x16 (&nxt)[QB], SoftState& s
   };
   bf16x8 kf[G::kDC];
   if (HAS_NEXT) {
-    kf[0] = kpre[0];
-    kf[1] = kpre[1];
+#pragma unroll
+    for (int r = 0; r < kRA; ++r) kf[r] = kpre[r];
   }
 #pragma unroll
   for (int i = 0; i < kA; ++i) {
     const int cc = i / QB, qb = i % QB;
     if (HAS_NEXT) {
-      if (qb == 0 && cc + 2 < G::kDC) kf[cc + 2] = kread(cc + 2);
+      if (qb == 0 && cc + kRA < G::kDC) kf[cc + kRA] = kread(cc + kRA);
       if (cc > 0)
         nxt[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cc], qf[qb][cc], nxt[qb], 0, 0, 0);
       else if (MASK_NEXT)
@@ -402,8 +414,9 @@ __device__ inline void step32(f32x16 (&cur)[QB], f32x16 (&nxt)[QB], SoftState& s
       pb[pq][pr >> 2][pr & 3] = word;
       ls[pq] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, word), ones, ls[pq], false);
     });
-    if (i == kA - 4) vf[0] = vread(0);
-    if (i == kA - 3) vf[1] = vread(1);
+#pragma unroll
+    for (int r = 0; r < kRA; ++r)
+      if (i == kA - 2 * kRA + r) vf[r] = vread(r);
     __builtin_amdgcn_sched_barrier(0);
   }
   // Keep the row sums in part A: an empty asm consuming them stops IR passes
@@ -420,7 +433,7 @@ __device__ inline void step32(f32x16 (&cur)[QB], f32x16 (&nxt)[QB], SoftState& s
   for (int i = 0; i < kB; ++i) {
     const int k = i / QB, qb = i % QB;
     const int u = k / G::kND, db = k % G::kND;
-    if (qb == 0 && k + 2 < kNV) vf[k + 2] = vread(k + 2);
+    if (qb == 0 && k + kRA < kNV) vf[k + kRA] = vread(k + kRA);
     acc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
         vf[k], __builtin_bit_cast(bf16x8, u32x4{pb[qb][u][0], pb[qb][u][1], pb[qb][u][2], pb[qb][u][3]}),
         acc[db][qb], 0, 0, 0);
@@ -429,8 +442,9 @@ __device__ inline void step32(f32x16 (&cur)[QB], f32x16 (&nxt)[QB], SoftState& s
         const int xq = w >> 3, xr = w & 7;
         mx[xq] = max3(mx[xq], nxt[xq][2 * xr], nxt[xq][2 * xr + 1]);
       });
-    if (PRE_NEXT && i == kB - 4) kpre[0] = k_frag<D>(kb_after, rk_after, 0, col, hf);
-    if (PRE_NEXT && i == kB - 3) kpre[1] = k_frag<D>(kb_after, rk_after, 1, col, hf);
+#pragma unroll
+    for (int r = 0; r < kRA; ++r)
+      if (PRE_NEXT && i == kB - 2 * kRA + r) kpre[r] = k_frag<D>(kb_after, rk_after, r, col, hf);
     __builtin_amdgcn_sched_barrier(0);
   }
   if (HAS_NEXT) update_ref(mx, st, c);
@@ -502,7 +516,6 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(
     load_k(j + 1);
     load_v(j);
   };
-
   load_k(0);
 #pragma unroll
   for (int j = 0; j < kLead; ++j) load_batch(j);
@@ -548,14 +561,31 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(
   block_max(sa, st, c);
   // K fragments of the next step's part A are read ahead, at the end of the
   // previous part B (that K tile has been resident since an earlier barrier).
-  bf16x8 kpre[2];
-  kpre[0] = k_frag<D>(kslot(0), 32, 0, col, hf);
-  kpre[1] = k_frag<D>(kslot(0), 32, 1, col, hf);
+  bf16x8 kpre[kRA];
+#pragma unroll
+  for (int r = 0; r < kRA; ++r) kpre[r] = k_frag<D>(kslot(0), 32, r, col, hf);
 
   // Tile t (64 keys) = two 32-key steps.  At its top batch t (K t+1, V t) has
   // landed, batches t+1 .. t+kLead-1 may still be in flight, and batch
   // t+kLead is issued into the slots tile t-1 released.
+  // Steady part: the tiles loaded (K t+kLead+1, V t+kLead) are full and not
+  // the last one, so their addresses simply advance by one tile per step.
+  const uint64_t tb = uint64_t(kBN) * uint64_t(rowbytes);
+  uint64_t kaddr = reinterpret_cast<uint64_t>(kh) + uint64_t(kLead + 1) * tb;
+  uint64_t vaddr = reinterpret_cast<uint64_t>(vh) + uint64_t(kLead) * tb;
   int t = 0;
+  for (; t <= nT - 3 - kLead; ++t) {
+    tile_barrier<kBatch * (kLead - 1)>();
+    kl.load_at(kaddr, kslot(t + kLead + 1), wave);
+    vl.load_at(vaddr, vslot(t + kLead), wave);
+    kaddr += tb;
+    vaddr += tb;
+    const char* vb = vslot(t);
+    char* kbc = kslot(t);
+    char* kbn = kslot(t + 1);
+    step32<D, true, false, true>(sa, sb, st, pb, acc, qf, kbc, 32, zero, vb, 0, c, lane, col, hf, kpre, kbn, 0);
+    step32<D, true, false, true>(sb, sa, st, pb, acc, qf, kbn, 0, zero, vb, 32, c, lane, col, hf, kpre, kbn, 32);
+  }
   for (; t < nT - 2; ++t) {  // the next tile is not the last one: no masking
     tile_barrier<kBatch * (kLead - 1)>();
     load_batch(t + kLead);
