@@ -42,6 +42,9 @@
 // of the row's position inside a tile.
 #include "internal.h"
 
+#include <type_traits>
+#include <utility>
+
 namespace spattn {
 namespace {
 
@@ -74,12 +77,19 @@ constexpr int kRA = SPATTN_RA;
 #define SPATTN_LEAD 2
 #endif
 constexpr int kLead = SPATTN_LEAD;     // K/V tiles in flight ahead of the tile being used
+#ifndef SPATTN_BN
+#define SPATTN_BN 64
+#endif
+constexpr int kBN = SPATTN_BN;         // keys per tile
+constexpr int kSteps = kBN / 32;       // 32-key steps per tile
+static_assert(kSteps % 2 == 0, "the two S^T register sets alternate within a tile");
 constexpr int pow2_ceil(int x) { return x <= 1 ? 1 : 2 * pow2_ceil((x + 1) / 2); }
-// Slot counts are rounded up to powers of two so that slot indices are masks.
-constexpr int kKSlots = pow2_ceil(kLead + 2);  // K: tiles t, t+1 read, t+2 .. t+1+kLead loading
-constexpr int kVSlots = pow2_ceil(kLead + 1);  // V: tile t read, t+1 .. t+kLead loading
-constexpr int kBN = 64;                // keys per tile
-constexpr int kKB = kBN / 32;          // 32-key blocks per tile
+// Slot counts are rounded up to powers of two (slot indices become masks)
+// when that still fits the 160 KiB of LDS.
+constexpr int slots(int n) { return (pow2_ceil(kLead + 2) + pow2_ceil(kLead + 1)) * kBN * 256 <= 160 * 1024
+                                        ? pow2_ceil(n) : n; }
+constexpr int kKSlots = slots(kLead + 2);  // K: tiles t, t+1 read, t+2 .. t+1+kLead loading
+constexpr int kVSlots = slots(kLead + 1);  // V: tile t read, t+1 .. t+kLead loading
 constexpr float kTau = 8.0f;           // lazy-rescale threshold (log2 units)
 constexpr float kLn2 = 0.69314718055994531f;
 
@@ -342,7 +352,7 @@ __device__ inline void slot_items(int i, F&& f) {
 }
 
 template <int D, bool HAS_NEXT, bool MASK_NEXT, bool PRE_NEXT>
-__device__ inline void step32(f32x16 (&cur)[QB], f32x16 (&nxt)[QB], SoftState& st, PW& pb,
+__device__ __attribute__((always_inline)) inline void step32(f32x16 (&cur)[QB], f32x16 (&nxt)[QB], SoftState& st, PW& pb,
                               f32x16 (&acc)[Geo<D>::kND][QB], const bf16x8 (&qf)[QB][Geo<D>::kDC],
                               const char* kb_next, int rk_next, const f32x16& init_next, const char* vb, int rv,
                               float c, int lane, int col, int hf, bf16x8 (&kpre)[kRA], const char* kb_after,
@@ -450,6 +460,13 @@ __device__ inline void step32(f32x16 (&cur)[QB], f32x16 (&nxt)[QB], SoftState& s
   if (HAS_NEXT) update_ref(mx, st, c);
 }
 
+// f(integral_constant<int, I>) for I = 0, 1, ...: a loop whose index is a
+// compile-time constant (the steps of a tile use it as a template argument).
+template <int... Is, typename Fn>
+__device__ __attribute__((always_inline)) inline void for_each_index(std::integer_sequence<int, Is...>, Fn&& f) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+
 // s_waitcnt immediate: vmcnt(vm), expcnt untouched, lgkmcnt(0).
 constexpr unsigned waitcnt_vm_lgkm0(unsigned vm) { return (vm & 0xFu) | ((vm >> 4) << 14) | (0x7u << 4); }
 
@@ -550,7 +567,6 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(
     st.alpha[qb] = 1.f;
   }
   const f32x16 zero = {};
-  const int last0 = (nT - 1) * kBN;  // first key of the last tile
 
   f32x16 sa[QB], sb[QB];  // S^T of the current / next 32 keys
   PW pb;
@@ -564,10 +580,42 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(
   bf16x8 kpre[kRA];
 #pragma unroll
   for (int r = 0; r < kRA; ++r) kpre[r] = k_frag<D>(kslot(0), 32, r, col, hf);
+  // Tile t (kBN keys) = kSteps 32-key steps.  At its top batch t (K t+1, V t)
+  // has landed, batches t+1 .. t+kLead-1 may still be in flight, and batch
+  // t+kLead is issued into the slots that tile t-1 released.
+  // The kSteps 32-key steps of tile t.  Step s holds S^T of block s of the
+  // tile, computes S^T of the next block (the following block of this tile,
+  // or block 0 of tile t+1) and reads ahead the first K fragments of the block
+  // after that.  LAST: t is the last tile; NEXT_LAST: tile t+1 is.
+  auto tile_steps = [&](int t, auto last_, auto next_last_) __attribute__((always_inline)) {
+    constexpr bool LAST = decltype(last_)::value;
+    constexpr bool NEXT_LAST = decltype(next_last_)::value;
+    const char* vb = vslot(t);
+    char* kc = kslot(t);
+    char* kn = kslot(t + 1);
+    auto one = [&](auto s_) __attribute__((always_inline)) {
+      constexpr int s = decltype(s_)::value;
+      constexpr bool next_in = s + 1 < kSteps, after_in = s + 2 < kSteps;
+      constexpr bool HAS_NEXT = next_in || !LAST;
+      constexpr bool MASK_NEXT = next_in ? LAST : NEXT_LAST;
+      constexpr bool PRE_NEXT = after_in || !LAST;
+      const char* kb_next = next_in ? kc : kn;
+      const char* kb_after = after_in ? kc : kn;
+      const int rk_next = next_in ? 32 * (s + 1) : 0;
+      const int rk_after = after_in ? 32 * (s + 2) : 32 * (s + 2 - kSteps);
+      const f32x16 init = MASK_NEXT ? tail_init(t * kBN + 32 * (s + 1), skv, hf) : zero;
+      if constexpr (s % 2 == 0)
+        step32<D, HAS_NEXT, MASK_NEXT, PRE_NEXT>(sa, sb, st, pb, acc, qf, kb_next, rk_next, init, vb, 32 * s, c,
+                                                 lane, col, hf, kpre, kb_after, rk_after);
+      else
+        step32<D, HAS_NEXT, MASK_NEXT, PRE_NEXT>(sb, sa, st, pb, acc, qf, kb_next, rk_next, init, vb, 32 * s, c,
+                                                 lane, col, hf, kpre, kb_after, rk_after);
+    };
+    for_each_index(std::make_integer_sequence<int, kSteps>{}, one);
+  };
+  using F = std::false_type;
+  using T = std::true_type;
 
-  // Tile t (64 keys) = two 32-key steps.  At its top batch t (K t+1, V t) has
-  // landed, batches t+1 .. t+kLead-1 may still be in flight, and batch
-  // t+kLead is issued into the slots tile t-1 released.
   // Steady part: the tiles loaded (K t+kLead+1, V t+kLead) are full and not
   // the last one, so their addresses simply advance by one tile per step.
   const uint64_t tb = uint64_t(kBN) * uint64_t(rowbytes);
@@ -580,41 +628,21 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(
     vl.load_at(vaddr, vslot(t + kLead), wave);
     kaddr += tb;
     vaddr += tb;
-    const char* vb = vslot(t);
-    char* kbc = kslot(t);
-    char* kbn = kslot(t + 1);
-    step32<D, true, false, true>(sa, sb, st, pb, acc, qf, kbc, 32, zero, vb, 0, c, lane, col, hf, kpre, kbn, 0);
-    step32<D, true, false, true>(sb, sa, st, pb, acc, qf, kbn, 0, zero, vb, 32, c, lane, col, hf, kpre, kbn, 32);
+    tile_steps(t, F{}, F{});
   }
   for (; t < nT - 2; ++t) {  // the next tile is not the last one: no masking
     tile_barrier<kBatch * (kLead - 1)>();
     load_batch(t + kLead);
-    const char* vb = vslot(t);
-    char* kbc = kslot(t);
-    char* kbn = kslot(t + 1);
-    step32<D, true, false, true>(sa, sb, st, pb, acc, qf, kbc, 32, zero, vb, 0, c, lane, col, hf, kpre, kbn, 0);
-    step32<D, true, false, true>(sb, sa, st, pb, acc, qf, kbn, 0, zero, vb, 32, c, lane, col, hf, kpre, kbn, 32);
+    tile_steps(t, F{}, F{});
   }
   if (t == nT - 2) {  // the next tile is the last one
     tile_barrier<kBatch * (kLead - 1)>();
     load_batch(t + kLead);
-    const char* vb = vslot(t);
-    char* kbc = kslot(t);
-    char* kbn = kslot(t + 1);
-    step32<D, true, false, true>(sa, sb, st, pb, acc, qf, kbc, 32, zero, vb, 0, c, lane, col, hf, kpre, kbn, 0);
-    step32<D, true, true, true>(sb, sa, st, pb, acc, qf, kbn, 0, tail_init(last0, skv, hf), vb, 32, c, lane, col,
-                                hf, kpre, kbn, 32);
+    tile_steps(t, F{}, T{});
     ++t;
   }
-  {  // last tile: no further loads are issued
-    tile_barrier<kBatch * (kLead - 1)>();
-    const char* vb = vslot(t);
-    char* kbc = kslot(t);
-    step32<D, true, true, false>(sa, sb, st, pb, acc, qf, kbc, 32, tail_init(last0 + 32, skv, hf), vb, 0, c, lane,
-                                 col, hf, kpre, nullptr, 0);
-    step32<D, false, false, false>(sb, sa, st, pb, acc, qf, nullptr, 0, zero, vb, 32, c, lane, col, hf, kpre,
-                                   nullptr, 0);
-  }
+  tile_barrier<kBatch * (kLead - 1)>();  // last tile: no further loads are issued
+  tile_steps(t, T{}, F{});
   // No LDS-direct load may still be landing once this work-group's LDS is
   // handed to the next one.
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
