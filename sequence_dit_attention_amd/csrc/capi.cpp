@@ -67,7 +67,7 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 int launch_copies(const std::vector<CopySeg>& segs, int64_t outer, void* stream) {
   if (segs.empty() || outer == 0) return ok();
-  hipGetLastError();  // launches below report their own status
+  (void)hipGetLastError();  // launches below report their own status
   hipError_t e = spattn::launch_segcopy(segs.data(), static_cast<int>(segs.size()), outer,
                                         as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "segmented copy launch");
@@ -212,7 +212,7 @@ int rope_apply(int32_t dtype, const void* x, void* y, int64_t s, int32_t H, int3
   if (!x || !y) return fail(SP_EINVAL, "rope_apply: null device pointer");
   if (x != y && ranges_overlap(x, bytes, y, bytes))
     return fail(SP_EOVERLAP, "rope_apply: x and y overlap without being equal");
-  hipGetLastError();
+  (void)hipGetLastError();
   hipError_t e = spattn::launch_rope(dtype, x, y, s, H, d, pos0, theta, style, as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "rope launch");
   return ok();
@@ -243,7 +243,7 @@ int shard_attn_fwd(int32_t dtype, const void* q, const void* k, const void* v, v
   if (lse && (ranges_overlap(lse, lb, q, qb) || ranges_overlap(lse, lb, k, kb) ||
               ranges_overlap(lse, lb, v, kb) || ranges_overlap(lse, lb, o, qb)))
     return fail(SP_EOVERLAP, "shard_attn_fwd: lse overlaps another buffer");
-  hipGetLastError();
+  (void)hipGetLastError();
   hipError_t e;
   if (dtype == SP_BF16)
     e = spattn::launch_attn_bf16(q, k, v, o, lse, sq, skv, H, d, scale, as_stream(stream));

@@ -5,15 +5,17 @@
 // sequence-major tensor (page "HCCL AllGatherV 实战解析：MiniMax-H3-Comfy-NPU ...",
 // section 后端 A).  Both reduce to a list of (src, dst, nbytes) copies, one per
 // (outer slice, rank).  The copy is HBM-bound: each work-group moves one
-// fixed 32 KiB chunk of one segment with 16-byte non-temporal loads issued
-// before the stores, so every lane keeps several requests in flight.
+// fixed 4 KiB chunk of one segment, one 16-byte non-temporal load and store
+// per lane.  Many small work-groups keep more requests in flight across the
+// chip than few large ones (on MI355X a 4.5 GB copy runs at about 6.5 TB/s
+// with 4 KiB chunks against 5.2 TB/s with 32 KiB chunks).
 #include "internal.h"
 
 namespace spattn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kVecs = 8;                                      // 16-byte vectors per lane
+constexpr int kVecs = 1;                                      // 16-byte vectors per lane
 constexpr int64_t kChunk = int64_t(kThreads) * kVecs * 16;    // bytes per work-group
 constexpr int kMaxSegs = 32;                                  // segments per launch
 constexpr int64_t kMaxGridY = 65535;
@@ -88,7 +90,7 @@ hipError_t launch_segcopy(const CopySeg* segs, int n, int64_t outer, hipStream_t
     a.first_blk[a.nseg] = blocks;
     if (a.nseg == 0) continue;
     // Grid x covers one outer slice; a segment beyond 2^31 chunks is not reachable
-    // (2^31 * 32 KiB = 64 TiB), so blocks always fits.
+    // (2^31 * 4 KiB = 8 TiB), so blocks always fits.
     for (int64_t o = 0; o < outer; o += kMaxGridY) {
       const unsigned gy = static_cast<unsigned>(min(kMaxGridY, outer - o));
       hipLaunchKernelGGL(segcopy_kernel, dim3(static_cast<unsigned>(blocks), gy), dim3(kThreads), 0,

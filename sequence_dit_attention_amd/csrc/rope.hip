@@ -53,32 +53,44 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(const T* x, T* y, int64_
     sn[u] = float(sv);
   }
 
-  for (int h = 0; h < H; ++h) {
-    const int64_t row = (t * H + h) * int64_t(d);
-    float a[PG], b[PG];
-    if (INTERLEAVED) {
+  // Heads are processed in batches of HB: all loads of a batch are issued
+  // before its stores.  x and y are either the same buffer or disjoint, and
+  // every element is read and written by this thread only, so reading ahead
+  // of the stores is safe in place too (the compiler cannot prove it, so the
+  // batching is explicit).
+  constexpr int HB = 8;
+  for (int h0 = 0; h0 < H; h0 += HB) {
+    float a[HB][PG], b[HB][PG];
+#pragma unroll
+    for (int hh = 0; hh < HB; ++hh) {
+      if (h0 + hh >= H) break;
+      const int64_t row = (t * H + h0 + hh) * int64_t(d);
 #pragma unroll
       for (int u = 0; u < PG; ++u) {
-        a[u] = ld(x + row + 2 * (j0 + u));
-        b[u] = ld(x + row + 2 * (j0 + u) + 1);
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < PG; ++u) {
-        a[u] = ld(x + row + j0 + u);
-        b[u] = ld(x + row + half + j0 + u);
+        if (INTERLEAVED) {
+          a[hh][u] = ld(x + row + 2 * (j0 + u));
+          b[hh][u] = ld(x + row + 2 * (j0 + u) + 1);
+        } else {
+          a[hh][u] = ld(x + row + j0 + u);
+          b[hh][u] = ld(x + row + half + j0 + u);
+        }
       }
     }
 #pragma unroll
-    for (int u = 0; u < PG; ++u) {
-      const float ya = a[u] * cs[u] - b[u] * sn[u];
-      const float yb = b[u] * cs[u] + a[u] * sn[u];
-      if (INTERLEAVED) {
-        st(y + row + 2 * (j0 + u), ya);
-        st(y + row + 2 * (j0 + u) + 1, yb);
-      } else {
-        st(y + row + j0 + u, ya);
-        st(y + row + half + j0 + u, yb);
+    for (int hh = 0; hh < HB; ++hh) {
+      if (h0 + hh >= H) break;
+      const int64_t row = (t * H + h0 + hh) * int64_t(d);
+#pragma unroll
+      for (int u = 0; u < PG; ++u) {
+        const float ya = a[hh][u] * cs[u] - b[hh][u] * sn[u];
+        const float yb = b[hh][u] * cs[u] + a[hh][u] * sn[u];
+        if (INTERLEAVED) {
+          st(y + row + 2 * (j0 + u), ya);
+          st(y + row + 2 * (j0 + u) + 1, yb);
+        } else {
+          st(y + row + j0 + u, ya);
+          st(y + row + half + j0 + u, yb);
+        }
       }
     }
   }
