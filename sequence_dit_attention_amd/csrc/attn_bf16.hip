@@ -74,7 +74,7 @@ constexpr int BM = kWaves * 32 * QB;   // query rows per work-group
 #endif
 constexpr int kRA = SPATTN_RA;
 #ifndef SPATTN_LEAD
-#define SPATTN_LEAD 2
+#define SPATTN_LEAD 1
 #endif
 constexpr int kLead = SPATTN_LEAD;     // K/V tiles in flight ahead of the tile being used
 #ifndef SPATTN_BN
