@@ -89,6 +89,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="p768_15s_w4")
     ap.add_argument("--cpu-rows", type=int, default=192, help="query rows in the CPU-oracle sample (0: skip)")
+    ap.add_argument("--gf-steps", type=int, default=2,
+                    help="steps of the gather-free variant timed after the headline steps (0: skip)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -155,6 +157,27 @@ def main() -> int:
     log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (host wall {wall / args.steps * 1e3:.3f} ms); "
         + ", ".join(f"{s} {t:.3f} ms" for s, t in per.items()))
 
+    # The gather-free variant of the same share (K/V read from the rank shards by
+    # the attention kernel, no pack/unpack); reported beside the headline step.
+    gf = None
+    if args.gf_steps > 0:
+        share.step_gather_free()
+        torch.cuda.synchronize()
+        g = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.gf_steps)]
+        for i in range(args.gf_steps):
+            g[i][0].record()
+            share.rope()
+            g[i][1].record()
+            share.attend_gather_free()
+            g[i][2].record()
+            share.concat_out()
+            g[i][3].record()
+        torch.cuda.synchronize()
+        gms = [sum(g[i][j].elapsed_time(g[i][j + 1]) for i in range(args.gf_steps)) / args.gf_steps for j in range(3)]
+        gf = {"ms_per_step": sum(gms), "rope_ms": gms[0], "attn_gv_ms": gms[1], "concat_out_ms": gms[2],
+              "attn_gv_tflops": share.attn_flops() / (gms[1] * 1e-3) / 1e12}
+        log(f"gather-free step: {sum(gms):.3f} ms (attention on the shards {gms[1]:.3f} ms)")
+
     flops = share.attn_flops()
     attn_tflops = flops / (per["attn"] * 1e-3) / 1e12
     pack_bytes = share.pack_kv_bytes()
@@ -185,6 +208,7 @@ def main() -> int:
             "rope_ms": per["rope"], "concat_out_ms": per["concat_out"],
             "attn_kernel_sha256_16": kernel_hash(),
         },
+        "gather_free": gf,
     }
     if args.cpu_rows > 0:
         log(f"CPU oracle baseline on {args.cpu_rows} rows")

@@ -172,6 +172,30 @@ int shard_attn_fwd(int32_t dtype, const void* q, const void* k, const void* v,
                    void* o, float* lse, int64_t sq, int64_t skv, int32_t H, int32_t d,
                    float scale, void* stream);
 
+/*
+ * shard_attn_fwd_gv -- shard_attn_fwd against K/V left in the W per-rank
+ * shards, without the gather into one buffer.  Section 后端 A reassembles
+ * the full sequence by concatenating the ranks' blocks in rank order; here
+ * the kernel reads each K/V tile straight from the shard that holds it, so
+ * the sequence is the same concatenation and the result is bit-identical to
+ * shard_attn_fwd on the gathered buffers (same keys, same order, same
+ * arithmetic).
+ *   q          device [sq, H, d]
+ *   W          number of shards, 1 <= W <= 16
+ *   k_shards, v_shards  host arrays of W device pointers; shard r is a
+ *              contiguous [seq_lens[r], H, d] tensor (may be NULL when
+ *              seq_lens[r] == 0)
+ *   seq_lens   host array of W token counts (>= 0, sum >= 1)
+ *   o, lse, sq, H, d, scale, stream  as in shard_attn_fwd
+ * Errors: as shard_attn_fwd, plus SP_EINVAL (W < 1, null host arrays, a
+ * negative length, a null shard with tokens), SP_EUNSUPPORTED (W > 16),
+ * SP_ERANGE (lengths overflow), SP_EOVERLAP (o or lse overlaps q, a shard or
+ * each other).  sq == 0 enqueues nothing.
+ */
+int shard_attn_fwd_gv(int32_t dtype, const void* q, int32_t W, const void* const* k_shards,
+                      const void* const* v_shards, const int64_t* seq_lens, void* o, float* lse,
+                      int64_t sq, int32_t H, int32_t d, float scale, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

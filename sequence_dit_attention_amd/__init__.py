@@ -9,6 +9,7 @@ from .api import (  # noqa: F401
     exchange_sim,
     rope_apply,
     shard_attn_fwd,
+    shard_attn_fwd_gv,
     sp_abi_version,
     sp_allgatherv_layout,
     sp_shard_bounds,

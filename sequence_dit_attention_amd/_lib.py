@@ -19,6 +19,8 @@ SIGNATURES = [
     ("rope_apply", ctypes.c_int, [_I32, _VP, _VP, _I64, _I32, _I32, _I64, ctypes.c_double, _I32, _VP]),
     ("shard_attn_fwd", ctypes.c_int, [_I32, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I32, _I32,
                                       ctypes.c_float, _VP]),
+    ("shard_attn_fwd_gv", ctypes.c_int, [_I32, _VP, _I32, ctypes.POINTER(_VP), ctypes.POINTER(_VP), _PI64,
+                                         _VP, _VP, _I64, _I32, _I32, ctypes.c_float, _VP]),
 ]
 
 _lib = None

@@ -152,3 +152,38 @@ def exchange_sim(shards, cat_dim: int = 0):
     out = torch.empty(shape, dtype=ref.dtype, device=ref.device)
     varlen_unpack(flat, displs, lens, outer, inner, out)
     return out
+
+
+def shard_attn_fwd_gv(q: torch.Tensor, k_shards, v_shards, out: torch.Tensor | None = None,
+                      lse: torch.Tensor | None = None, scale: float | None = None) -> torch.Tensor:
+    """shard_attn_fwd of q [sq, H, d] against K/V given as per-rank shards [s_r, H, d] (sequence =
+    their concatenation in rank order), read in place without a gather."""
+    if q.dim() != 3:
+        raise ValueError("q must be [sq, H, d]")
+    W = len(k_shards)
+    if len(v_shards) != W or W < 1:
+        raise ValueError("k_shards and v_shards must be non-empty lists of equal length")
+    sq, H, d = q.shape
+    for kt, vt in zip(k_shards, v_shards):
+        if kt.dim() != 3 or kt.shape != vt.shape or kt.shape[1:] != (H, d):
+            raise ValueError("every shard must be [s_r, H, d] with q's H and d, K and V alike")
+        if kt.dtype != q.dtype or vt.dtype != q.dtype:
+            raise TypeError("shard dtype differs from q")
+    if out is None:
+        out = torch.empty_like(q)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    lp = None
+    if lse is not None:
+        if lse.dtype != torch.float32 or lse.shape != (H, sq):
+            raise ValueError("lse must be float32 [H, sq]")
+        lp = _dev(lse, "lse")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    kp = (ctypes.c_void_p * W)(*[(_dev(t, "k shard") if t.numel() else None) for t in k_shards])
+    vp = (ctypes.c_void_p * W)(*[(_dev(t, "v shard") if t.numel() else None) for t in v_shards])
+    lens = (ctypes.c_int64 * W)(*[int(t.shape[0]) for t in k_shards])
+    check("shard_attn_fwd_gv", lib().shard_attn_fwd_gv(_dtype_code(q), _dev(q, "q"), W, kp, vp, lens,
+                                                       _dev(out, "out"), lp, sq, H, d, float(scale),
+                                                       _stream(q)))
+    return out

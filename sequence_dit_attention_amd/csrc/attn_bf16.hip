@@ -177,6 +177,33 @@ struct TileLoader {
 #pragma unroll
     for (int i = 0; i < G::kLoads; ++i) issue(rs, lds + (wave * G::kLoads + i) * 1024, voff[i]);
   }
+  // Tile whose first row is at `base` (wave-uniform); rows >= valid re-read
+  // row valid-1 (see load_clamped).
+  __device__ void load_base(const char* base, int valid, int64_t rowbytes, char* lds, int wave) const {
+    const i32x4 rs = rsrc(base);
+#pragma unroll
+    for (int i = 0; i < G::kLoads; ++i) {
+      const int over = rows[i] >= valid ? rows[i] - (valid - 1) : 0;
+      issue(rs, lds + (wave * G::kLoads + i) * 1024, voff[i] - uint32_t(over * rowbytes));
+    }
+  }
+  // Tile whose rows come from several shards: every lane finds the shard of
+  // its own row and loads from a 64-bit address.
+  __device__ void load_gather(const KvShards& kv, const void* const* ptr, int64_t hoff, int key0, int keyL,
+                              int64_t rowbytes, char* lds, int wave) const {
+#pragma unroll
+    for (int i = 0; i < G::kLoads; ++i) {
+      const int key = min(key0 + rows[i], keyL);
+      int r = 0;
+      for (int b = 1; b < kv.W; ++b) r += kv.start[b] <= key ? 1 : 0;
+      const uint32_t chunk = voff[i] - uint32_t(rows[i] * rowbytes);
+      const uint64_t addr = reinterpret_cast<uint64_t>(ptr[r]) + uint64_t(hoff) +
+                            uint64_t(key - kv.start[r]) * uint64_t(rowbytes) + chunk;
+      const uint32_t m0 =
+          __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>(lds + (wave * G::kLoads + i) * 1024)));
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(m0), "v"(addr) : "memory", "m0");
+    }
+  }
   // Last tile of a ragged sequence: rows >= skv re-read row skv-1 (finite data;
   // those keys are masked to -inf, so they carry zero weight).
   __device__ void load_clamped(const uint16_t* hb, int tile, int skv, int64_t rowbytes, char* lds,
@@ -483,10 +510,19 @@ __device__ inline void tile_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads) void attn_bf16_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    uint16_t* __restrict__ o, float* __restrict__ lse, int sq, int skv, int H, float c, int nqt) {
+// K/V argument of the kernel: one gathered [skv, H, d] buffer each, or a
+// table of per-rank shards (GV).
+struct KvFlat {
+  const uint16_t* k;
+  const uint16_t* v;
+};
+template <bool GV>
+using KvArg = typename std::conditional<GV, KvShards, KvFlat>::type;
+
+template <int D, bool GV>
+__global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const uint16_t* __restrict__ q, const KvArg<GV> kv,
+                                                             uint16_t* __restrict__ o, float* __restrict__ lse,
+                                                             int sq, int skv, int H, float c, int nqt) {
   using G = Geo<D>;
   // K tile j lives in slot j mod kKSlots, V tile j in slot j mod kVSlots.
   __shared__ __attribute__((aligned(1024))) char smem[(kKSlots + kVSlots) * G::kTileB];
@@ -505,8 +541,12 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(
   const int hf = lane >> 5;
   const int64_t rowstride = int64_t(H) * D;
   const int64_t rowbytes = rowstride * 2;
-  const uint16_t* kh = k + int64_t(h) * D;
-  const uint16_t* vh = v + int64_t(h) * D;
+  const uint16_t* kh = nullptr;
+  const uint16_t* vh = nullptr;
+  if constexpr (!GV) {
+    kh = kv.k + int64_t(h) * D;
+    vh = kv.v + int64_t(h) * D;
+  }
   const int nT = (skv + kBN - 1) / kBN;
   const bool ragged = (skv % kBN) != 0;
 
@@ -518,14 +558,51 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(
   auto vslot = [&](int j) { return vbase + (j % kVSlots) * G::kTileB; };
   // Tile indices past the end are clamped: those loads land in slots no live
   // tile uses and keep every batch the same size for the vmcnt accounting.
+  // Sharded K/V: a cursor per stream (K, V) follows the shard that holds the
+  // tiles being loaded (tiles are requested in increasing order).  A tile
+  // inside one shard is loaded like a gathered one from that shard's base; a
+  // tile across shard boundaries (at most W-1 per stream) takes the per-lane
+  // path.
+  struct Cursor {
+    int r;           // shard holding the last tile's first key
+    int s0, s1;      // its token range [s0, s1)
+    const char* p;   // its base pointer, offset to head h
+  };
+  const int64_t hoff = int64_t(h) * D * 2;
+  Cursor kcur{0, 0, 0, nullptr}, vcur{0, 0, 0, nullptr};
+  if constexpr (GV) {
+    kcur = Cursor{0, 0, int(kv.start[1]), static_cast<const char*>(kv.k[0]) + hoff};
+    vcur = Cursor{0, 0, int(kv.start[1]), static_cast<const char*>(kv.v[0]) + hoff};
+  }
+  auto load_sharded = [&](const auto& ld, const void* const* ptr, Cursor& cu, int tile, char* lds) {
+    if constexpr (GV) {
+      const int key0 = tile * kBN;
+      const int keyL = min(key0 + kBN, skv) - 1;
+      while (key0 >= cu.s1) {  // wave-uniform; empty shards are stepped over
+        ++cu.r;
+        cu.s0 = cu.s1;
+        cu.s1 = int(kv.start[cu.r + 1]);
+        cu.p = static_cast<const char*>(ptr[cu.r]) + hoff;
+      }
+      if (keyL < cu.s1) {
+        const char* base = cu.p + int64_t(key0 - cu.s0) * rowbytes;
+        if (keyL - key0 + 1 == kBN) ld.load_at(reinterpret_cast<uint64_t>(base), lds, wave);
+        else ld.load_base(base, keyL - key0 + 1, rowbytes, lds, wave);
+      } else {
+        ld.load_gather(kv, ptr, hoff, key0, keyL, rowbytes, lds, wave);
+      }
+    }
+  };
   auto load_k = [&](int j) {
     const int tile = min(j, nT - 1);
-    if (ragged && tile == nT - 1) kl.load_clamped(kh, tile, skv, rowbytes, kslot(j), wave);
+    if constexpr (GV) load_sharded(kl, kv.k, kcur, tile, kslot(j));
+    else if (ragged && tile == nT - 1) kl.load_clamped(kh, tile, skv, rowbytes, kslot(j), wave);
     else kl.load(kh, tile, rowbytes, kslot(j), wave);
   };
   auto load_v = [&](int j) {
     const int tile = min(j, nT - 1);
-    if (ragged && tile == nT - 1) vl.load_clamped(vh, tile, skv, rowbytes, vslot(j), wave);
+    if constexpr (GV) load_sharded(vl, kv.v, vcur, tile, vslot(j));
+    else if (ragged && tile == nT - 1) vl.load_clamped(vh, tile, skv, rowbytes, vslot(j), wave);
     else vl.load(vh, tile, rowbytes, vslot(j), wave);
   };
   // Batch j = {K tile j+1, V tile j}; tile t needs batch t.
@@ -624,8 +701,13 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(
   int t = 0;
   for (; t <= nT - 3 - kLead; ++t) {
     tile_barrier<kBatch * (kLead - 1)>();
-    kl.load_at(kaddr, kslot(t + kLead + 1), wave);
-    vl.load_at(vaddr, vslot(t + kLead), wave);
+    if constexpr (GV) {
+      load_sharded(kl, kv.k, kcur, t + kLead + 1, kslot(t + kLead + 1));
+      load_sharded(vl, kv.v, vcur, t + kLead, vslot(t + kLead));
+    } else {
+      kl.load_at(kaddr, kslot(t + kLead + 1), wave);
+      vl.load_at(vaddr, vslot(t + kLead), wave);
+    }
     kaddr += tb;
     vaddr += tb;
     tile_steps(t, F{}, F{});
@@ -670,15 +752,14 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(
   }
 }
 
-template <int D>
-hipError_t launch_d(const void* q, const void* k, const void* v, void* o, float* lse, int64_t sq, int64_t skv,
-                    int H, float c, hipStream_t stream) {
+template <int D, bool GV>
+hipError_t launch_d(const void* q, const KvArg<GV>& kv, void* o, float* lse, int64_t sq, int64_t skv, int H,
+                    float c, hipStream_t stream) {
   const int64_t nqt = (sq + BM - 1) / BM;
   const int64_t grid = nqt * H;
   if (grid > kMaxGrid) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((attn_bf16_kernel<D>), dim3(unsigned(grid)), dim3(kThreads), 0, stream,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, int(sq), int(skv), H, c,
+  hipLaunchKernelGGL((attn_bf16_kernel<D, GV>), dim3(unsigned(grid)), dim3(kThreads), 0, stream,
+                     static_cast<const uint16_t*>(q), kv, static_cast<uint16_t*>(o), lse, int(sq), int(skv), H, c,
                      int(nqt));
   return hipGetLastError();
 }
@@ -689,8 +770,18 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o
                             int64_t skv, int H, int d, float scale, hipStream_t stream) {
   if (sq > (int64_t(1) << 31) - 1024) return hipErrorInvalidValue;
   const float c = scale * 1.4426950408889634f;
-  if (d == 64) return launch_d<64>(q, k, v, o, lse, sq, skv, H, c, stream);
-  return launch_d<128>(q, k, v, o, lse, sq, skv, H, c, stream);
+  const KvFlat kv{static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v)};
+  if (d == 64) return launch_d<64, false>(q, kv, o, lse, sq, skv, H, c, stream);
+  return launch_d<128, false>(q, kv, o, lse, sq, skv, H, c, stream);
+}
+
+hipError_t launch_attn_bf16_gv(const void* q, const KvShards& kv, void* o, float* lse, int64_t sq, int H, int d,
+                               float scale, hipStream_t stream) {
+  if (sq > (int64_t(1) << 31) - 1024) return hipErrorInvalidValue;
+  const float c = scale * 1.4426950408889634f;
+  const int64_t skv = kv.start[kv.W];
+  if (d == 64) return launch_d<64, true>(q, kv, o, lse, sq, skv, H, c, stream);
+  return launch_d<128, true>(q, kv, o, lse, sq, skv, H, c, stream);
 }
 
 }  // namespace spattn

@@ -8,19 +8,27 @@
 // folded into log2(e).
 #include "internal.h"
 
+#include <type_traits>
+
 namespace spattn {
 namespace {
 
 constexpr int kRows = 64;  // query rows (lanes) per work-group: one wave
 constexpr int kBN = 32;    // keys per LDS tile
 
-template <int D>
-__global__ __launch_bounds__(kRows) void attn_f32_kernel(const float* __restrict__ q,
-                                                         const float* __restrict__ k,
-                                                         const float* __restrict__ v, float* __restrict__ o,
-                                                         float* __restrict__ lse, int64_t sq, int64_t skv,
-                                                         int H, float c /* scale * log2(e) */,
-                                                         int64_t nqt) {
+// K/V argument: gathered [skv, H, d] buffers, or per-rank shards (GV).
+struct KvFlatF32 {
+  const float* k;
+  const float* v;
+};
+template <bool GV>
+using KvArgF32 = typename std::conditional<GV, KvShards, KvFlatF32>::type;
+
+template <int D, bool GV>
+__global__ __launch_bounds__(kRows) void attn_f32_kernel(const float* __restrict__ q, const KvArgF32<GV> kv,
+                                                         float* __restrict__ o, float* __restrict__ lse,
+                                                         int64_t sq, int64_t skv, int H,
+                                                         float c /* scale * log2(e) */, int64_t nqt) {
   __shared__ float ks[kBN][D];
   __shared__ float vs[kBN][D];
   const int64_t wg = blockIdx.x;
@@ -42,8 +50,21 @@ __global__ __launch_bounds__(kRows) void attn_f32_kernel(const float* __restrict
     for (int idx = threadIdx.x; idx < kBN * D; idx += kRows) {
       const int r = idx / D, e = idx % D;
       const int64_t j = j0 + r;
-      ks[r][e] = j < skv ? k[(j * H + h) * D + e] : 0.f;
-      vs[r][e] = j < skv ? v[(j * H + h) * D + e] : 0.f;
+      float kx = 0.f, vx = 0.f;
+      if (j < skv) {
+        if constexpr (GV) {  // shard s holds tokens [start[s], start[s+1])
+          int s = 0;
+          for (int b = 1; b < kv.W; ++b) s += kv.start[b] <= j ? 1 : 0;
+          const int64_t off = ((j - kv.start[s]) * H + h) * D + e;
+          kx = static_cast<const float*>(kv.k[s])[off];
+          vx = static_cast<const float*>(kv.v[s])[off];
+        } else {
+          kx = kv.k[(j * H + h) * D + e];
+          vx = kv.v[(j * H + h) * D + e];
+        }
+      }
+      ks[r][e] = kx;
+      vs[r][e] = vx;
     }
     __syncthreads();
     float sc[kBN];
@@ -82,21 +103,32 @@ __global__ __launch_bounds__(kRows) void attn_f32_kernel(const float* __restrict
   if (lse) lse[int64_t(h) * sq + i] = (m + log2f(l)) * 0.69314718055994531f;
 }
 
-}  // namespace
-
-hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float* o, float* lse,
-                           int64_t sq, int64_t skv, int H, int d, float scale, hipStream_t stream) {
+template <bool GV>
+hipError_t launch_any(const float* q, const KvArgF32<GV>& kv, float* o, float* lse, int64_t sq, int64_t skv,
+                      int H, int d, float scale, hipStream_t stream) {
   const int64_t nqt = (sq + kRows - 1) / kRows;
   const int64_t grid = nqt * H;
   if (grid > kMaxGrid) return hipErrorInvalidConfiguration;
   const float c = scale * 1.4426950408889634f;
   if (d == 64)
-    hipLaunchKernelGGL(attn_f32_kernel<64>, dim3(unsigned(grid)), dim3(kRows), 0, stream, q, k, v, o, lse,
-                       sq, skv, H, c, nqt);
+    hipLaunchKernelGGL((attn_f32_kernel<64, GV>), dim3(unsigned(grid)), dim3(kRows), 0, stream, q, kv, o, lse, sq,
+                       skv, H, c, nqt);
   else
-    hipLaunchKernelGGL(attn_f32_kernel<128>, dim3(unsigned(grid)), dim3(kRows), 0, stream, q, k, v, o,
-                       lse, sq, skv, H, c, nqt);
+    hipLaunchKernelGGL((attn_f32_kernel<128, GV>), dim3(unsigned(grid)), dim3(kRows), 0, stream, q, kv, o, lse,
+                       sq, skv, H, c, nqt);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                           int64_t sq, int64_t skv, int H, int d, float scale, hipStream_t stream) {
+  return launch_any<false>(q, KvFlatF32{k, v}, o, lse, sq, skv, H, d, scale, stream);
+}
+
+hipError_t launch_attn_f32_gv(const float* q, const KvShards& kv, float* o, float* lse, int64_t sq, int H, int d,
+                              float scale, hipStream_t stream) {
+  return launch_any<true>(q, kv, o, lse, sq, kv.start[kv.W], H, d, scale, stream);
 }
 
 }  // namespace spattn

@@ -76,6 +76,32 @@ int launch_copies(const std::vector<CopySeg>& segs, int64_t outer, void* stream)
 
 }  // namespace
 
+namespace {
+
+// Checks shared by both attention entry points; fills the byte sizes of q/o,
+// of all K (or V) tokens, and of lse.
+int check_attn(const char* fn, int32_t dtype, int64_t sq, int64_t skv, int32_t H, int32_t d, float scale,
+               int64_t* qb, int64_t* kb, int64_t* lb) {
+  const int eb = elem_bytes(dtype);
+  if (!eb) return fail(SP_EINVAL, "%s: unknown dtype %d", fn, dtype);
+  if (sq < 0 || skv < 1 || H < 1) return fail(SP_EINVAL, "%s: need sq >= 0, skv >= 1, H >= 1", fn);
+  if (d != 64 && d != 128) return fail(SP_EUNSUPPORTED, "%s: head size %d not supported (64, 128)", fn, d);
+  if (!(std::isfinite(scale) && scale > 0.f)) return fail(SP_EINVAL, "%s: scale must be finite and > 0", fn);
+  int64_t qn, kn;
+  if (!mul_ok(sq, int64_t(H) * d, &qn) || !mul_ok(skv, int64_t(H) * d, &kn) || !mul_ok(qn, eb, qb) ||
+      !mul_ok(kn, eb, kb) || !mul_ok(sq, int64_t(H) * 4, lb))
+    return fail(SP_ERANGE, "%s: size overflows int64", fn);
+  // Grid: one work-group per (32-query tile, head) at most; keep it inside 2^31.
+  if ((sq + 31) / 32 > spattn::kMaxGrid / H) return fail(SP_ERANGE, "%s: sq*H too large for one launch", fn);
+  if (skv > (int64_t(1) << 31) - 256) return fail(SP_ERANGE, "%s: skv must be < 2^31", fn);
+  // The kernels address a 64-token K/V tile with 32-bit byte offsets.
+  if (int64_t(H) * d * 4 * 64 > (int64_t(1) << 31) - 1)
+    return fail(SP_ERANGE, "%s: H*d too large (64 tokens of K must span < 2 GiB)", fn);
+  return SP_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int sp_abi_version(void) { return SPATTN_ABI_VERSION; }
@@ -218,24 +244,11 @@ int rope_apply(int32_t dtype, const void* x, void* y, int64_t s, int32_t H, int3
   return ok();
 }
 
+
 int shard_attn_fwd(int32_t dtype, const void* q, const void* k, const void* v, void* o, float* lse,
                    int64_t sq, int64_t skv, int32_t H, int32_t d, float scale, void* stream) {
-  const int eb = elem_bytes(dtype);
-  if (!eb) return fail(SP_EINVAL, "shard_attn_fwd: unknown dtype %d", dtype);
-  if (sq < 0 || skv < 1 || H < 1) return fail(SP_EINVAL, "shard_attn_fwd: need sq >= 0, skv >= 1, H >= 1");
-  if (d != 64 && d != 128) return fail(SP_EUNSUPPORTED, "shard_attn_fwd: head size %d not supported (64, 128)", d);
-  if (!(std::isfinite(scale) && scale > 0.f)) return fail(SP_EINVAL, "shard_attn_fwd: scale must be finite and > 0");
-  int64_t qn, kn, qb, kb, lb;
-  if (!mul_ok(sq, int64_t(H) * d, &qn) || !mul_ok(skv, int64_t(H) * d, &kn) || !mul_ok(qn, eb, &qb) ||
-      !mul_ok(kn, eb, &kb) || !mul_ok(sq, int64_t(H) * 4, &lb))
-    return fail(SP_ERANGE, "shard_attn_fwd: size overflows int64");
-  // Grid: one work-group per (32-query tile, head) at most; keep it inside 2^31.
-  if ((sq + 31) / 32 > spattn::kMaxGrid / H)
-    return fail(SP_ERANGE, "shard_attn_fwd: sq*H too large for one launch");
-  if (skv > (int64_t(1) << 31) - 256) return fail(SP_ERANGE, "shard_attn_fwd: skv must be < 2^31");
-  // The kernels address a 64-token K/V tile with 32-bit byte offsets.
-  if (int64_t(H) * d * 4 * 64 > (int64_t(1) << 31) - 1)
-    return fail(SP_ERANGE, "shard_attn_fwd: H*d too large (64 tokens of K must span < 2 GiB)");
+  int64_t qb, kb, lb;
+  if (int rc = check_attn("shard_attn_fwd", dtype, sq, skv, H, d, scale, &qb, &kb, &lb)) return rc;
   if (sq == 0) return ok();
   if (!q || !k || !v || !o) return fail(SP_EINVAL, "shard_attn_fwd: null device pointer");
   if (ranges_overlap(o, qb, q, qb) || ranges_overlap(o, qb, k, kb) || ranges_overlap(o, qb, v, kb))
@@ -251,6 +264,52 @@ int shard_attn_fwd(int32_t dtype, const void* q, const void* k, const void* v, v
     e = spattn::launch_attn_f32(static_cast<const float*>(q), static_cast<const float*>(k),
                                 static_cast<const float*>(v), static_cast<float*>(o), lse, sq, skv, H,
                                 d, scale, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return ok();
+}
+
+int shard_attn_fwd_gv(int32_t dtype, const void* q, int32_t W, const void* const* k_shards,
+                      const void* const* v_shards, const int64_t* seq_lens, void* o, float* lse, int64_t sq,
+                      int32_t H, int32_t d, float scale, void* stream) {
+  const char* fn = "shard_attn_fwd_gv";
+  if (W < 1) return fail(SP_EINVAL, "%s: W must be >= 1", fn);
+  if (W > spattn::kMaxShards) return fail(SP_EUNSUPPORTED, "%s: at most %d shards", fn, spattn::kMaxShards);
+  if (!k_shards || !v_shards || !seq_lens) return fail(SP_EINVAL, "%s: null host array", fn);
+  spattn::KvShards kv{};
+  kv.W = W;
+  kv.start[0] = 0;
+  for (int32_t r = 0; r < W; ++r) {
+    if (seq_lens[r] < 0) return fail(SP_EINVAL, "%s: seq_lens[%d] < 0", fn, r);
+    if (!add_ok(kv.start[r], seq_lens[r], &kv.start[r + 1])) return fail(SP_ERANGE, "%s: sum of seq_lens overflows", fn);
+    kv.k[r] = k_shards[r];
+    kv.v[r] = v_shards[r];
+  }
+  const int64_t skv = kv.start[W];
+  int64_t qb, kb, lb;
+  if (int rc = check_attn(fn, dtype, sq, skv, H, d, scale, &qb, &kb, &lb)) return rc;
+  if (sq == 0) return ok();
+  if (!q || !o) return fail(SP_EINVAL, "%s: null device pointer", fn);
+  const int64_t tok_bytes = int64_t(H) * d * elem_bytes(dtype);
+  if (ranges_overlap(o, qb, q, qb)) return fail(SP_EOVERLAP, "%s: o overlaps q", fn);
+  if (lse && (ranges_overlap(lse, lb, q, qb) || ranges_overlap(lse, lb, o, qb)))
+    return fail(SP_EOVERLAP, "%s: lse overlaps another buffer", fn);
+  for (int32_t r = 0; r < W; ++r) {
+    const int64_t nb = seq_lens[r] * tok_bytes;  // <= kb, no overflow
+    if (nb == 0) continue;
+    if (!kv.k[r] || !kv.v[r]) return fail(SP_EINVAL, "%s: null shard %d with %lld tokens", fn, r,
+                                          static_cast<long long>(seq_lens[r]));
+    if (ranges_overlap(o, qb, kv.k[r], nb) || ranges_overlap(o, qb, kv.v[r], nb))
+      return fail(SP_EOVERLAP, "%s: o overlaps shard %d", fn, r);
+    if (lse && (ranges_overlap(lse, lb, kv.k[r], nb) || ranges_overlap(lse, lb, kv.v[r], nb)))
+      return fail(SP_EOVERLAP, "%s: lse overlaps shard %d", fn, r);
+  }
+  (void)hipGetLastError();
+  hipError_t e;
+  if (dtype == SP_BF16)
+    e = spattn::launch_attn_bf16_gv(q, kv, o, lse, sq, H, d, scale, as_stream(stream));
+  else
+    e = spattn::launch_attn_f32_gv(static_cast<const float*>(q), kv, static_cast<float*>(o), lse, sq, H, d, scale,
+                                   as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return ok();
 }

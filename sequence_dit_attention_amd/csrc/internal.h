@@ -30,6 +30,24 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o
 hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                            int64_t sq, int64_t skv, int H, int d, float scale, hipStream_t stream);
 
+// K/V given as W per-rank shards instead of one gathered buffer: shard r
+// holds tokens [start[r], start[r+1]) of the sequence as a contiguous
+// [start[r+1] - start[r], H, d] tensor (k[r], v[r] may be null when empty).
+constexpr int kMaxShards = 16;
+struct KvShards {
+  const void* k[kMaxShards];
+  const void* v[kMaxShards];
+  int64_t start[kMaxShards + 1];
+  int W;
+};
+
+// Attention against sharded K/V (same results as the gathered call on the
+// concatenation of the shards).
+hipError_t launch_attn_bf16_gv(const void* q, const KvShards& kv, void* o, float* lse, int64_t sq, int H, int d,
+                               float scale, hipStream_t stream);
+hipError_t launch_attn_f32_gv(const float* q, const KvShards& kv, float* o, float* lse, int64_t sq, int H, int d,
+                              float scale, hipStream_t stream);
+
 // Largest grid (work-groups) the attention launchers accept.
 constexpr int64_t kMaxGrid = (int64_t(1) << 31) - 1;
 

@@ -80,6 +80,11 @@ class RankShare:
         api.shard_attn_fwd(self.q_rot, self.k_full, self.v_full, out=self.o_shards[self.r],
                            lse=self.lse, scale=self.scale)
 
+    def attend_gather_free(self) -> None:
+        """Attention reading K/V from the rank shards in place (no pack/unpack)."""
+        api.shard_attn_fwd_gv(self.q_rot, self.k_rot, self.v_shards, out=self.o_shards[self.r],
+                              lse=self.lse, scale=self.scale)
+
     def concat_out(self) -> None:
         api.varlen_pack([t.view(-1) for t in self.o_shards], self.counts, self.displs, self.flat_o)
         api.varlen_unpack(self.flat_o, self.displs, self.lens, 1, self.inner, self.o_full)
@@ -88,6 +93,12 @@ class RankShare:
         self.rope()
         self.gather_kv()
         self.attend()
+        self.concat_out()
+
+    def step_gather_free(self) -> None:
+        """The same share without the K/V gather: attention reads the shards directly."""
+        self.rope()
+        self.attend_gather_free()
         self.concat_out()
 
     # -- algorithmic work of one step -------------------------------------------------

@@ -27,7 +27,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert "shard_attn_fwd" in names and len(names) == 8
+    assert "shard_attn_fwd" in names and "shard_attn_fwd_gv" in names and len(names) == 9
     h = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
         assert hasattr(h, n), n
@@ -121,6 +121,30 @@ def test_attn_validation():
     assert f(1, q, k, v, o, o + 8, 10, 20, 2, 128, 0.1, None) == SP_EOVERLAP
     assert f(1, None, k, v, o, None, 10, 20, 2, 128, 0.1, None) == SP_EINVAL
     assert f(1, q, k, v, o, None, 0, 20, 2, 128, 0.1, None) == 0   # sq == 0: nothing enqueued
+
+
+def test_attn_gv_validation():
+    L = _lib.lib()
+    f = L.shard_attn_fwd_gv
+    q, o = FAKE, FAKE * 4
+    P = ctypes.c_void_p
+
+    def call(W, ks, vs, lens, qq=q, oo=o, lse=None, sq=10, H=2, d=128, scale=0.1, dtype=1):
+        return f(dtype, qq, W, (P * len(ks))(*ks), (P * len(vs))(*vs), _arr(lens), oo, lse, sq, H, d, scale, None)
+
+    ks, vs = [FAKE * 2, FAKE * 2 + 10_000], [FAKE * 3, FAKE * 3 + 10_000]
+    assert call(0, ks, vs, [5, 6]) == SP_EINVAL                          # W
+    assert call(17, ks * 9, vs * 9, [1] * 18) == SP_EUNSUPPORTED        # too many shards
+    assert call(2, ks, vs, [5, -1]) == SP_EINVAL                         # negative length
+    assert call(2, ks, vs, [0, 0]) == SP_EINVAL                          # empty sequence
+    assert call(2, ks, vs, [5, 6], d=96) == SP_EUNSUPPORTED
+    assert call(2, [FAKE * 2, None], vs, [5, 6]) == SP_EINVAL            # null shard with tokens
+    assert call(2, ks, vs, [5, 6], oo=FAKE * 2 + 512) == SP_EOVERLAP     # o over a K shard
+    assert call(2, ks, vs, [5, 6], lse=FAKE * 3 + 64) == SP_EOVERLAP     # lse over a V shard
+    assert call(2, ks, vs, [5, 6], oo=q + 64) == SP_EOVERLAP             # o over q
+    assert f(1, q, 2, None, (P * 2)(*vs), _arr([5, 6]), o, None, 10, 2, 128, 0.1, None) == SP_EINVAL
+    assert call(2, ks, vs, [5, 6], sq=0) == 0                            # nothing enqueued
+    assert call(2, [None, FAKE * 2], [None, FAKE * 3], [0, 6], sq=0) == 0
 
 
 def test_python_wrapper_raises():
