@@ -322,35 +322,6 @@ __device__ inline void rescale_o(f32x16 (&o)[Geo<D>::kND][QB], const float (&alp
       for (int r = 0; r < 16; ++r) o[db][qb][r] *= alpha[qb];
 }
 
-// O^T += V^T P^T over the 32 keys at rows r0 .. r0+31 of an LDS V tile.  MFMA u
-// contracts keys r0 + 16u + {4hf..4hf+3, 8+4hf..8+4hf+3} in k-slots 8hf..8hf+7,
-// the order in which the S^T accumulator holds them.
-template <int D>
-__device__ inline void pv32(f32x16 (&o)[Geo<D>::kND][QB], const PW& pb, const char* vb, int r0, int lane,
-                            int hf) {
-  using G = Geo<D>;
-  const int g16 = lane >> 4, j16 = lane & 15;
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int ra = r0 + 16 * u + 4 * hf + (j16 >> 2);
-#pragma unroll
-    for (int db = 0; db < G::kND; ++db) {
-      const int dcol = db * 32 + 16 * (g16 & 1) + 4 * (j16 & 3);
-      const int ch = dcol >> 3, inb = (dcol & 7) * 2;
-      const char* p0 = vb + ra * G::kRowB + ((ch ^ G::swz_v(ra)) << 4) + inb;
-      const char* p1 = vb + (ra + 8) * G::kRowB + ((ch ^ G::swz_v(ra + 8)) << 4) + inb;
-      const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
-      const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p1);
-      const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-        o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            a, __builtin_bit_cast(bf16x8, u32x4{pb[qb][u][0], pb[qb][u][1], pb[qb][u][2], pb[qb][u][3]}),
-            o[db][qb], 0, 0, 0);
-    }
-  }
-}
-
 // One 32-key step, issued in a fixed order: every MFMA is followed by its
 // share of the VALU work and a scheduling fence, so the SIMD's in-order issue
 // alternates matrix and vector instructions (an MFMA occupies the matrix pipe
