@@ -17,6 +17,8 @@ from .spattn_oracle import (  # noqa: F401
     varlen_unpack,
     rope_inv_freq,
     rope_apply,
+    rope_apply_mx,
+    av_positions,
     attention,
     attention_rows,
     output_concat,

@@ -161,6 +161,68 @@ def rope_apply(x: np.ndarray, pos0: int, theta: float = 10000.0, style: str = "h
     return y
 
 
+def rope_apply_mx(x: np.ndarray, pos: np.ndarray, sections, theta: float = 10000.0,
+                  style: str = "half") -> np.ndarray:
+    """Multi-axis rotary embedding of x [s, H, d] with explicit positions.
+
+    The pages slice a RoPE frequency table by the rank's token range [MH3, 机制一]
+    without defining it; this is the multi-axis form used for packed video
+    tokens (the reading is stated in the design notes; parity unpinned by the
+    pages).  The d/2 pairs are split into consecutive groups of sections[a]
+    pairs, one per axis a; pair j' of axis a (0-based inside its group)
+    rotates by pos[token, a] * theta**(-2 j' / d_a) with d_a = 2 * sections[a].
+    Pairing and the rotation formula are those of rope_apply.  Float64.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    s, H, d = x.shape
+    pos = np.asarray(pos, dtype=np.float64).reshape(s, len(sections))
+    if d % 2 or sum(sections) != d // 2:
+        raise ValueError("sections must add up to d/2 pairs")
+    ang = np.empty((s, d // 2), dtype=np.float64)
+    j0 = 0
+    for a, n in enumerate(sections):
+        if n:
+            ang[:, j0:j0 + n] = pos[:, a:a + 1] * rope_inv_freq(2 * n, theta)[None, :]
+        j0 += n
+    cos = np.cos(ang)[:, None, :]
+    sin = np.sin(ang)[:, None, :]
+    if style == "half":
+        x1, x2 = x[..., : d // 2], x[..., d // 2:]
+    elif style == "interleaved":
+        x1, x2 = x[..., 0::2], x[..., 1::2]
+    else:
+        raise ValueError("style must be 'half' or 'interleaved'")
+    y = np.empty_like(x)
+    y1 = x1 * cos - x2 * sin
+    y2 = x2 * cos + x1 * sin
+    if style == "half":
+        y[..., : d // 2], y[..., d // 2:] = y1, y2
+    else:
+        y[..., 0::2], y[..., 1::2] = y1, y2
+    return y
+
+
+def av_positions(T: int, Hh: int, Ww: int, n_audio: int, a: int, b: int) -> np.ndarray:
+    """Axis positions [b - a, 3] of tokens [a, b) of a packed video + audio sequence.
+
+    Video tokens come first, frame-major then row-major (token i < T*Hh*Ww is
+    frame i // (Hh*Ww), row (i // Ww) % Hh, column i % Ww); the n_audio audio
+    tokens follow and take a 1-D position, their index among the audio tokens,
+    on the first axis (0 on the others).  Reading of the packed layout
+    (video then audio in one index) stated in the design notes.
+    """
+    V = T * Hh * Ww
+    if not (0 <= a <= b <= V + n_audio):
+        raise ValueError("token range outside the sequence")
+    out = np.zeros((b - a, 3), dtype=np.int64)
+    for k, i in enumerate(range(a, b)):
+        if i < V:
+            out[k] = (i // (Hh * Ww), (i // Ww) % Hh, i % Ww)
+        else:
+            out[k, 0] = i - V
+    return out
+
+
 # ---------------------------------------------------------------------------
 # Attention of local queries against the full sequence  [MH3, 机制一; HY3]
 # ---------------------------------------------------------------------------
