@@ -101,6 +101,7 @@ def main() -> int:
     import numpy as np
     import torch
 
+    from sequence_dit_attention_amd import api
     from sequence_dit_attention_amd.pipeline import RankShare
     from synth import gen_qkv, get_workload
 
@@ -178,6 +179,36 @@ def main() -> int:
               "attn_gv_tflops": share.attn_flops() / (gms[1] * 1e-3) / 1e12}
         log(f"gather-free step: {sum(gms):.3f} ms (attention on the shards {gms[1]:.3f} ms)")
 
+    # Multi-axis RoPE of the rank's Q slice with the packed video+audio positions of
+    # the 768P/15 s grid (reported beside the headline step; not part of it).
+    rmx = None
+    grid = {"p768_15s_w4": (91, 48, 84, 375), "p768_5s_w4": (31, 48, 84, 125)}.get(wl.name)
+    if grid is not None:
+        T, Hh, Ww, A = grid
+        V = T * Hh * Ww
+        pos = api.sp_av_positions(T, Hh, Ww, A, share.a, share.b).to(share.q_rot.device)
+        nv = max(0, min(share.b, V) - share.a)
+        sec_video = (wl.d // 2 - 2 * (wl.d // 6), wl.d // 6, wl.d // 6)
+        xq = torch.empty_like(share.q_rot)
+
+        def rope_mx():
+            if nv:
+                api.rope_apply_mx(share.q[share.a:share.a + nv], pos[:nv], sec_video, wl.theta, out=xq[:nv])
+            if nv < share.b - share.a:
+                api.rope_apply_mx(share.q[share.a + nv:share.b], pos[nv:], (wl.d // 2, 0, 0), wl.theta,
+                                  out=xq[nv:])
+        rope_mx()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            rope_mx()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 5
+        rmx = {"q_ms": ms, "gbs": 2 * xq.numel() * xq.element_size() / (ms * 1e-3) / 1e9,
+               "sections_video": sec_video, "grid": {"T": T, "H": Hh, "W": Ww, "audio": A}}
+
     flops = share.attn_flops()
     attn_tflops = flops / (per["attn"] * 1e-3) / 1e12
     pack_bytes = share.pack_kv_bytes()
@@ -209,6 +240,7 @@ def main() -> int:
             "attn_kernel_sha256_16": kernel_hash(),
         },
         "gather_free": gf,
+        "rope_multi_axis": rmx,
     }
     if args.cpu_rows > 0:
         log(f"CPU oracle baseline on {args.cpu_rows} rows")

@@ -147,6 +147,39 @@ int rope_apply(int32_t dtype, const void* x, void* y, int64_t s, int32_t H, int3
                int64_t pos0, double theta, int32_t style, void* stream);
 
 /*
+ * rope_apply_mx -- multi-axis rotary embedding with explicit positions.
+ * Section 机制一 slices "the RoPE frequency table" with the rank's token
+ * range without defining the table; for packed video tokens the table is
+ * read here as the usual multi-axis form.  The d/2 pairs (paired as in
+ * rope_apply) are split into consecutive groups of sections[0], sections[1]
+ * and sections[2] pairs, one per axis; pair j' of axis a (0-based inside its
+ * group) rotates by phi = pos[t][a] * theta^(-2 j' / (2 sections[a])).  With
+ * sections = {d/2, 0, 0} and pos[t][0] = pos0 + t this is rope_apply
+ * (same arithmetic, same bits).  Precision as rope_apply.
+ *   x, y       device [s, H, d] of dtype; y == x allowed, other overlap not
+ *   pos        device int64 [s, 3]: token t's position on each axis; values
+ *              must satisfy |pos| < 2^53 (device data, not checked)
+ *   sections   host array of 3 pair counts, each >= 0, summing to d/2
+ * Errors: as rope_apply, plus SP_EINVAL (null or invalid sections, null pos
+ * with s > 0) and SP_EOVERLAP (pos overlaps y).
+ */
+int rope_apply_mx(int32_t dtype, const void* x, void* y, int64_t s, int32_t H, int32_t d,
+                  const int64_t* pos, const int32_t* sections, double theta, int32_t style, void* stream);
+
+/*
+ * sp_av_positions -- axis positions of tokens [a, b) of a packed video+audio
+ * sequence (host).  The packed sequence of section 机制一 holds the video
+ * tokens of a T x Hh x Ww latent grid (frame-major, then row-major) followed
+ * by n_audio audio tokens.  Video token i gets (i / (Hh*Ww), (i / Ww) % Hh,
+ * i % Ww); audio token i gets (i - T*Hh*Ww, 0, 0), a 1-D position meant for
+ * rope_apply_mx with sections {d/2, 0, 0}.
+ *   out   host array of 3*(b-a) int64 values, written by the call
+ * Errors: SP_EINVAL (negative sizes, a range outside [0, T*Hh*Ww + n_audio),
+ * null out with b > a), SP_ERANGE (grid size overflows int64).  Host-only.
+ */
+int sp_av_positions(int64_t T, int64_t Hh, int64_t Ww, int64_t n_audio, int64_t a, int64_t b, int64_t* out);
+
+/*
  * shard_attn_fwd -- attention of the rank's local queries against the full
  * gathered sequence.  Section 机制一: Q comes from the local shard while K/V
  * must cover the whole sequence.  Unmasked (bidirectional) softmax attention:

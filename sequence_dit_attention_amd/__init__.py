@@ -8,10 +8,12 @@ from .api import (  # noqa: F401
     SP_F32,
     exchange_sim,
     rope_apply,
+    rope_apply_mx,
     shard_attn_fwd,
     shard_attn_fwd_gv,
     sp_abi_version,
     sp_allgatherv_layout,
+    sp_av_positions,
     sp_shard_bounds,
     varlen_pack,
     varlen_unpack,

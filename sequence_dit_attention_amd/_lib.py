@@ -17,6 +17,9 @@ SIGNATURES = [
     ("varlen_pack", ctypes.c_int, [_I32, _I32, ctypes.POINTER(_VP), _PI64, _PI64, _VP, _I64, _VP]),
     ("varlen_unpack", ctypes.c_int, [_I32, _I32, _VP, _I64, _PI64, _PI64, _I64, _I64, _VP, _VP]),
     ("rope_apply", ctypes.c_int, [_I32, _VP, _VP, _I64, _I32, _I32, _I64, ctypes.c_double, _I32, _VP]),
+    ("rope_apply_mx", ctypes.c_int, [_I32, _VP, _VP, _I64, _I32, _I32, _VP, ctypes.POINTER(ctypes.c_int32),
+                                     ctypes.c_double, _I32, _VP]),
+    ("sp_av_positions", ctypes.c_int, [_I64, _I64, _I64, _I64, _I64, _I64, _PI64]),
     ("shard_attn_fwd", ctypes.c_int, [_I32, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I32, _I32,
                                       ctypes.c_float, _VP]),
     ("shard_attn_fwd_gv", ctypes.c_int, [_I32, _VP, _I32, ctypes.POINTER(_VP), ctypes.POINTER(_VP), _PI64,

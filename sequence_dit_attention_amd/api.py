@@ -106,6 +106,32 @@ def rope_apply(x: torch.Tensor, pos0: int, theta: float = 10000.0, style: str = 
     return y
 
 
+def rope_apply_mx(x: torch.Tensor, pos: torch.Tensor, sections, theta: float = 10000.0, style: str = "half",
+                  out: torch.Tensor | None = None) -> torch.Tensor:
+    """Multi-axis RoPE of x [s, H, d] with positions pos (device int64 [s, 3]) and pairs per axis
+    `sections` (3 ints summing to d/2); in place when out is None or out is x."""
+    if x.dim() != 3:
+        raise ValueError("x must be [s, H, d]")
+    y = x if out is None else out
+    if y.shape != x.shape or y.dtype != x.dtype:
+        raise ValueError("out must match x in shape and dtype")
+    s, H, d = x.shape
+    if pos.dtype != torch.int64 or tuple(pos.shape) != (s, 3):
+        raise ValueError("pos must be int64 [s, 3]")
+    sec = (ctypes.c_int32 * 3)(*[int(v) for v in sections])
+    check("rope_apply_mx", lib().rope_apply_mx(_dtype_code(x), _dev(x, "x"), _dev(y, "out"), s, H, d,
+                                               _dev(pos, "pos"), sec, float(theta), _STYLES[style], _stream(x)))
+    return y
+
+
+def sp_av_positions(T: int, Hh: int, Ww: int, n_audio: int, a: int, b: int) -> torch.Tensor:
+    """Axis positions (host int64 tensor [b - a, 3]) of tokens [a, b) of a packed video + audio sequence."""
+    outn = max(b - a, 0)
+    arr = (ctypes.c_int64 * (3 * outn if outn else 1))()
+    check("sp_av_positions", lib().sp_av_positions(T, Hh, Ww, n_audio, a, b, arr))
+    return torch.tensor(list(arr)[: 3 * outn], dtype=torch.int64).reshape(outn, 3)
+
+
 def shard_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor | None = None,
                    lse: torch.Tensor | None = None, scale: float | None = None) -> torch.Tensor:
     """Attention of q [sq, H, d] against k, v [skv, H, d]; returns O [sq, H, d] (lse [H, sq] if given)."""

@@ -244,6 +244,57 @@ int rope_apply(int32_t dtype, const void* x, void* y, int64_t s, int32_t H, int3
   return ok();
 }
 
+int rope_apply_mx(int32_t dtype, const void* x, void* y, int64_t s, int32_t H, int32_t d, const int64_t* pos,
+                  const int32_t* sections, double theta, int32_t style, void* stream) {
+  const char* fn = "rope_apply_mx";
+  const int eb = elem_bytes(dtype);
+  if (!eb) return fail(SP_EINVAL, "%s: unknown dtype %d", fn, dtype);
+  if (style != SP_ROPE_HALF && style != SP_ROPE_INTERLEAVED) return fail(SP_EINVAL, "%s: unknown style %d", fn, style);
+  if (s < 0 || H < 1) return fail(SP_EINVAL, "%s: need s >= 0 and H >= 1", fn);
+  if (d < 2 || d > 1024 || (d & 1)) return fail(SP_EINVAL, "%s: d must be even, 2..1024 (got %d)", fn, d);
+  if (!(std::isfinite(theta) && theta > 0.0)) return fail(SP_EINVAL, "%s: theta must be finite and > 0", fn);
+  if (!sections) return fail(SP_EINVAL, "%s: null sections", fn);
+  if (sections[0] < 0 || sections[1] < 0 || sections[2] < 0 || sections[0] + sections[1] + sections[2] != d / 2)
+    return fail(SP_EINVAL, "%s: sections must be >= 0 and add up to d/2 = %d pairs", fn, d / 2);
+  int64_t n, bytes, pbytes;
+  if (!mul_ok(s, int64_t(H) * d, &n) || !mul_ok(n, eb, &bytes) || !mul_ok(s, 3 * 8, &pbytes))
+    return fail(SP_ERANGE, "%s: size overflows int64", fn);
+  if (n == 0) return ok();
+  if (!x || !y || !pos) return fail(SP_EINVAL, "%s: null device pointer", fn);
+  if (x != y && ranges_overlap(x, bytes, y, bytes)) return fail(SP_EOVERLAP, "%s: x and y overlap without being equal", fn);
+  if (ranges_overlap(pos, pbytes, y, bytes)) return fail(SP_EOVERLAP, "%s: positions overlap y", fn);
+  const int sec[3] = {sections[0], sections[1], sections[2]};
+  (void)hipGetLastError();
+  hipError_t e = spattn::launch_rope_mx(dtype, x, y, s, H, d, pos, sec, theta, style, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "rope launch");
+  return ok();
+}
+
+int sp_av_positions(int64_t T, int64_t Hh, int64_t Ww, int64_t n_audio, int64_t a, int64_t b, int64_t* out) {
+  const char* fn = "sp_av_positions";
+  if (T < 0 || Hh < 0 || Ww < 0 || n_audio < 0) return fail(SP_EINVAL, "%s: negative grid size", fn);
+  int64_t hw, V, S;
+  if (!mul_ok(Hh, Ww, &hw) || !mul_ok(T, hw, &V) || !add_ok(V, n_audio, &S))
+    return fail(SP_ERANGE, "%s: grid size overflows int64", fn);
+  if (a < 0 || a > b || b > S) return fail(SP_EINVAL, "%s: token range [%lld, %lld) outside [0, %lld)", fn,
+                                           static_cast<long long>(a), static_cast<long long>(b),
+                                           static_cast<long long>(S));
+  if (b > a && !out) return fail(SP_EINVAL, "%s: null output", fn);
+  for (int64_t i = a; i < b; ++i) {
+    int64_t* o = out + (i - a) * 3;
+    if (i < V) {
+      o[0] = i / hw;
+      o[1] = (i / Ww) % Hh;
+      o[2] = i % Ww;
+    } else {
+      o[0] = i - V;
+      o[1] = 0;
+      o[2] = 0;
+    }
+  }
+  return ok();
+}
+
 
 int shard_attn_fwd(int32_t dtype, const void* q, const void* k, const void* v, void* o, float* lse,
                    int64_t sq, int64_t skv, int32_t H, int32_t d, float scale, void* stream) {

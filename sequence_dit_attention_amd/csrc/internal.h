@@ -24,6 +24,10 @@ hipError_t launch_segcopy(const CopySeg* segs, int n, int64_t outer, hipStream_t
 hipError_t launch_rope(int dtype, const void* x, void* y, int64_t s, int H, int d,
                        int64_t pos0, double theta, int style, hipStream_t stream);
 
+// Multi-axis RoPE with explicit positions pos[s][3] (device) and pairs per axis sections[3] (host).
+hipError_t launch_rope_mx(int dtype, const void* x, void* y, int64_t s, int H, int d, const int64_t* pos,
+                          const int* sections, double theta, int style, hipStream_t stream);
+
 // Attention of q[sq, H, d] against k, v[skv, H, d].
 hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                             int64_t sq, int64_t skv, int H, int d, float scale, hipStream_t stream);

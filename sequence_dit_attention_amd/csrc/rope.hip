@@ -32,9 +32,15 @@ __device__ inline void st(uint16_t* p, float f) { *p = to_bf16(f); }
 
 // PG pairs per thread; element loads/stores are PG (or 2*PG) contiguous values
 // and the compiler merges them into vector accesses when aligned.
+// Multi-axis form: the d/2 pairs are split into consecutive groups of n0, n1
+// and d/2-n0-n1 pairs (axes 0, 1, 2); pair j' of axis a rotates by
+// pos[t][a] * theta^(-2 j' / (2 n_a)).  With pos == nullptr the single axis
+// position pos0 + t is used and the caller passes n0 = d/2, n1 = 0 (plain 1-D
+// RoPE, the same arithmetic as before).
 template <typename T, int PG, bool INTERLEAVED>
-__global__ __launch_bounds__(kThreads) void rope_kernel(const T* x, T* y, int64_t s,
-                                                        int H, int d, int64_t pos0, double log2theta) {
+__global__ __launch_bounds__(kThreads) void rope_kernel(const T* x, T* y, int64_t s, int H, int d, int64_t pos0,
+                                                        const int64_t* __restrict__ pos, int n0, int n1,
+                                                        double log2theta) {
   const int half = d >> 1;
   const int groups = half / PG;
   const int64_t g = int64_t(blockIdx.x) * kThreads + threadIdx.x;
@@ -43,10 +49,14 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(const T* x, T* y, int64_
   const int j0 = int(g - t * groups) * PG;
 
   float cs[PG], sn[PG];
-  const double p = double(pos0 + t);
 #pragma unroll
   for (int u = 0; u < PG; ++u) {
-    const double inv = exp2(-double(2 * (j0 + u)) / double(d) * log2theta);
+    const int j = j0 + u;
+    const int a = j < n0 ? 0 : (j < n0 + n1 ? 1 : 2);
+    const int jl = j - (a == 0 ? 0 : (a == 1 ? n0 : n0 + n1));      // index inside the axis group
+    const int da = 2 * (a == 0 ? n0 : (a == 1 ? n1 : half - n0 - n1));  // 2 * pairs of the axis
+    const double p = pos ? double(pos[t * 3 + a]) : double(pos0 + t);
+    const double inv = exp2(-double(2 * jl) / double(da) * log2theta);
     double sv, cv;
     sincos(p * inv, &sv, &cv);
     cs[u] = float(cv);
@@ -97,25 +107,25 @@ __global__ __launch_bounds__(kThreads) void rope_kernel(const T* x, T* y, int64_
 }
 
 template <typename T, int PG, bool IL>
-hipError_t launch_typed(const void* x, void* y, int64_t s, int H, int d, int64_t pos0, double l2t,
-                        hipStream_t stream) {
+hipError_t launch_typed(const void* x, void* y, int64_t s, int H, int d, int64_t pos0, const int64_t* pos, int n0,
+                        int n1, double l2t, hipStream_t stream) {
   const int64_t threads = s * ((d / 2) / PG);
   const int64_t blocks = (threads + kThreads - 1) / kThreads;
   if (blocks > kMaxGrid) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((rope_kernel<T, PG, IL>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
-                     stream, static_cast<const T*>(x), static_cast<T*>(y), s, H, d, pos0, l2t);
+                     stream, static_cast<const T*>(x), static_cast<T*>(y), s, H, d, pos0, pos, n0, n1, l2t);
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t launch_dtype(const void* x, void* y, int64_t s, int H, int d, int64_t pos0, double l2t,
-                        int style, hipStream_t stream) {
+hipError_t launch_dtype(const void* x, void* y, int64_t s, int H, int d, int64_t pos0, const int64_t* pos, int n0,
+                        int n1, double l2t, int style, hipStream_t stream) {
   const bool wide = ((d / 2) % 4) == 0;
   if (style == 1)
-    return wide ? launch_typed<T, 4, true>(x, y, s, H, d, pos0, l2t, stream)
-                : launch_typed<T, 1, true>(x, y, s, H, d, pos0, l2t, stream);
-  return wide ? launch_typed<T, 4, false>(x, y, s, H, d, pos0, l2t, stream)
-              : launch_typed<T, 1, false>(x, y, s, H, d, pos0, l2t, stream);
+    return wide ? launch_typed<T, 4, true>(x, y, s, H, d, pos0, pos, n0, n1, l2t, stream)
+                : launch_typed<T, 1, true>(x, y, s, H, d, pos0, pos, n0, n1, l2t, stream);
+  return wide ? launch_typed<T, 4, false>(x, y, s, H, d, pos0, pos, n0, n1, l2t, stream)
+              : launch_typed<T, 1, false>(x, y, s, H, d, pos0, pos, n0, n1, l2t, stream);
 }
 
 }  // namespace
@@ -123,8 +133,16 @@ hipError_t launch_dtype(const void* x, void* y, int64_t s, int H, int d, int64_t
 hipError_t launch_rope(int dtype, const void* x, void* y, int64_t s, int H, int d, int64_t pos0,
                        double theta, int style, hipStream_t stream) {
   const double l2t = log2(theta);
-  if (dtype == 0) return launch_dtype<float>(x, y, s, H, d, pos0, l2t, style, stream);
-  return launch_dtype<uint16_t>(x, y, s, H, d, pos0, l2t, style, stream);
+  if (dtype == 0) return launch_dtype<float>(x, y, s, H, d, pos0, nullptr, d / 2, 0, l2t, style, stream);
+  return launch_dtype<uint16_t>(x, y, s, H, d, pos0, nullptr, d / 2, 0, l2t, style, stream);
+}
+
+hipError_t launch_rope_mx(int dtype, const void* x, void* y, int64_t s, int H, int d, const int64_t* pos,
+                          const int* sections, double theta, int style, hipStream_t stream) {
+  const double l2t = log2(theta);
+  if (dtype == 0)
+    return launch_dtype<float>(x, y, s, H, d, 0, pos, sections[0], sections[1], l2t, style, stream);
+  return launch_dtype<uint16_t>(x, y, s, H, d, 0, pos, sections[0], sections[1], l2t, style, stream);
 }
 
 }  // namespace spattn

@@ -7,6 +7,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import oracle
@@ -27,7 +28,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert "shard_attn_fwd" in names and "shard_attn_fwd_gv" in names and len(names) == 9
+    assert "shard_attn_fwd" in names and "shard_attn_fwd_gv" in names and len(names) == 11
     h = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
         assert hasattr(h, n), n
@@ -106,6 +107,35 @@ def test_rope_validation():
     assert L.rope_apply(1, FAKE, FAKE, 10, 0, 8, 0, 1e4, 0, None) == SP_EINVAL      # H
     assert L.rope_apply(1, FAKE, FAKE, 10, 2, 8, 2**53, 1e4, 0, None) == SP_EINVAL  # positions
     assert L.rope_apply(1, FAKE, FAKE + 2, 10, 2, 8, 0, 1e4, 0, None) == SP_EOVERLAP
+
+
+def test_rope_mx_validation():
+    L = _lib.lib()
+    sec = (ctypes.c_int32 * 3)(2, 1, 1)
+    f = L.rope_apply_mx
+    bad = (ctypes.c_int32 * 3)(2, 1, 2)
+    assert f(1, FAKE, FAKE, 10, 2, 8, FAKE * 2, bad, 1e4, 0, None) == SP_EINVAL          # sections != d/2
+    neg = (ctypes.c_int32 * 3)(5, -1, 0)
+    assert f(1, FAKE, FAKE, 10, 2, 8, FAKE * 2, neg, 1e4, 0, None) == SP_EINVAL
+    assert f(1, FAKE, FAKE, 10, 2, 8, FAKE * 2, None, 1e4, 0, None) == SP_EINVAL         # null sections
+    assert f(1, FAKE, FAKE, 10, 2, 8, None, sec, 1e4, 0, None) == SP_EINVAL              # null positions
+    assert f(1, FAKE, FAKE, 10, 2, 7, FAKE * 2, sec, 1e4, 0, None) == SP_EINVAL          # odd d
+    assert f(1, FAKE, FAKE + 2, 10, 2, 8, FAKE * 2, sec, 1e4, 0, None) == SP_EOVERLAP    # partial x/y overlap
+    assert f(1, FAKE, FAKE, 10, 2, 8, FAKE + 16, sec, 1e4, 0, None) == SP_EOVERLAP       # positions inside y
+    assert f(1, FAKE, FAKE, 0, 2, 8, None, sec, 1e4, 0, None) == 0                        # s == 0: nothing to do
+
+
+def test_av_positions_match_oracle():
+    for T, Hh, Ww, A, a, b in [(3, 4, 5, 7, 0, 67), (3, 4, 5, 7, 13, 61), (91, 48, 84, 375, 91000, 91900),
+                               (91, 48, 84, 375, 366900, 367287), (2, 1, 1, 0, 0, 2), (0, 3, 3, 4, 0, 4)]:
+        got = api.sp_av_positions(T, Hh, Ww, A, a, b).numpy()
+        assert np.array_equal(got, oracle.av_positions(T, Hh, Ww, A, a, b))
+    L = _lib.lib()
+    out = (ctypes.c_int64 * 3)()
+    assert L.sp_av_positions(3, 4, 5, 7, 0, 68, out) == SP_EINVAL   # past the end
+    assert L.sp_av_positions(-1, 4, 5, 7, 0, 1, out) == SP_EINVAL
+    assert L.sp_av_positions(2**40, 2**20, 2**10, 0, 0, 1, out) == SP_ERANGE
+    assert L.sp_av_positions(3, 4, 5, 7, 0, 1, None) == SP_EINVAL
 
 
 def test_attn_validation():
