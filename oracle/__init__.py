@@ -19,6 +19,8 @@ from .spattn_oracle import (  # noqa: F401
     rope_apply,
     rope_apply_mx,
     av_positions,
+    rms_norm,
+    qk_norm_rope,
     attention,
     attention_rows,
     output_concat,

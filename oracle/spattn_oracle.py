@@ -202,6 +202,33 @@ def rope_apply_mx(x: np.ndarray, pos: np.ndarray, sections, theta: float = 10000
     return y
 
 
+def rms_norm(x: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """RMSNorm over the last axis: x / sqrt(mean(x**2) + eps) * gamma, float64.
+
+    [HY3] section "RmsNorm算子优化": RmsNorm is LayerNorm without the mean
+    subtraction.  gamma has one weight per feature (the head dimension here).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + np.float64(eps)) * np.asarray(gamma, dtype=np.float64)
+
+
+def qk_norm_rope(x: np.ndarray, gamma: np.ndarray, eps: float, pos0: int = 0, pos=None, sections=None,
+                 theta: float = 10000.0, style: str = "half") -> np.ndarray:
+    """Per-head RMSNorm of q or k followed by the rotary embedding, float64.
+
+    [HY3] section "计算分解": after the merged QKV projection the query and key
+    heads are normalised and rotated before attention (the page's "Q和V" is
+    read as Q and K: the rotation applies to q and k, section
+    消除旋转位置编码冗余cast算子).  One axis with positions pos0 + t when pos is
+    None, else the multi-axis form of rope_apply_mx.
+    """
+    xn = rms_norm(x, gamma, eps)
+    if pos is None:
+        return rope_apply(xn, pos0, theta, style)
+    return rope_apply_mx(xn, pos, sections, theta, style)
+
+
 def av_positions(T: int, Hh: int, Ww: int, n_audio: int, a: int, b: int) -> np.ndarray:
     """Axis positions [b - a, 3] of tokens [a, b) of a packed video + audio sequence.
 
