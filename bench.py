@@ -103,7 +103,7 @@ def main() -> int:
 
     from sequence_dit_attention_amd import api
     from sequence_dit_attention_amd.pipeline import RankShare
-    from synth import gen_qkv, get_workload
+    from synth import gen_gamma, gen_qkv, get_workload
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -209,6 +209,23 @@ def main() -> int:
         rmx = {"q_ms": ms, "gbs": 2 * xq.numel() * xq.element_size() / (ms * 1e-3) / 1e9,
                "sections_video": sec_video, "grid": {"T": T, "H": Hh, "W": Ww, "audio": A}}
 
+    # Per-head RMSNorm fused with RoPE on the rank's Q slice at its absolute 1-D
+    # positions (the step's RoPE with the q/k norm folded in; reported beside it).
+    gamma = torch.from_numpy(gen_gamma(wl.seed, wl.d)).to(share.q_rot.device)
+    xn = torch.empty_like(share.q_rot)
+    qsl = share.q[share.a:share.b]
+    api.qk_norm_rope(qsl, gamma, 1e-6, share.a, theta=wl.theta, out=xn)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        api.qk_norm_rope(qsl, gamma, 1e-6, share.a, theta=wl.theta, out=xn)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 5
+    qn_gbs = 2 * xn.numel() * xn.element_size() / (ms * 1e-3) / 1e9
+    qnr = {"q_ms": ms, "gbs": qn_gbs, "frac_hbm_peak": qn_gbs / PEAK_HBM_GBS, "eps": 1e-6}
+
     flops = share.attn_flops()
     attn_tflops = flops / (per["attn"] * 1e-3) / 1e12
     pack_bytes = share.pack_kv_bytes()
@@ -241,6 +258,7 @@ def main() -> int:
         },
         "gather_free": gf,
         "rope_multi_axis": rmx,
+        "qk_norm_rope": qnr,
     }
     if args.cpu_rows > 0:
         log(f"CPU oracle baseline on {args.cpu_rows} rows")

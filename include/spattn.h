@@ -167,6 +167,33 @@ int rope_apply_mx(int32_t dtype, const void* x, void* y, int64_t s, int32_t H, i
                   const int64_t* pos, const int32_t* sections, double theta, int32_t style, void* stream);
 
 /*
+ * qk_norm_rope -- per-head RMSNorm of q or k fused with the rotary embedding.
+ * Page "NPU HunyuanImage-3.0模型推理优化实践", section 计算分解: after the merged
+ * QKV projection the query and key heads are normalised and then rotated
+ * before attention; section RmsNorm算子优化: RMSNorm is LayerNorm without the
+ * mean subtraction.  For each token t and head h, over the d features of the
+ * head row:
+ *   n = x * gamma / sqrt(sum(x^2) / d + eps),   y = rope(n)
+ * where rope is rope_apply at positions pos0 + t when pos is NULL, else
+ * rope_apply_mx with pos and sections.  Norm and rotation are float32 (the
+ * angles float64, as in rope_apply); y is rounded once to dtype
+ * (nearest-even).  With eps = 0 an all-zero row gives NaN, as the formula.
+ *   x, y      device [s, H, d] of dtype; y == x allowed, other overlap not
+ *   gamma     device float32 [d]: the learned weight, shared by all heads
+ *   eps       added to the mean square; finite, >= 0 (applied in float32)
+ *   pos0      first token's position when pos is NULL (ignored otherwise)
+ *   pos       NULL, or device int64 [s, 3] as in rope_apply_mx
+ *   sections  host array of 3 pair counts (only read when pos is not NULL)
+ * Errors: as rope_apply / rope_apply_mx, plus SP_EINVAL (eps negative or not
+ * finite, null gamma with data), SP_EUNSUPPORTED (d/2 not splittable into at
+ * most 64 lanes of 1, 2, 4 or 8 pairs: every even d up to 128, every d up to
+ * 1024 with d/2 a multiple of 8), SP_EOVERLAP (gamma or pos overlaps y).
+ */
+int qk_norm_rope(int32_t dtype, const void* x, void* y, int64_t s, int32_t H, int32_t d, const float* gamma,
+                 double eps, int64_t pos0, const int64_t* pos, const int32_t* sections, double theta, int32_t style,
+                 void* stream);
+
+/*
  * sp_av_positions -- axis positions of tokens [a, b) of a packed video+audio
  * sequence (host).  The packed sequence of section 机制一 holds the video
  * tokens of a T x Hh x Ww latent grid (frame-major, then row-major) followed

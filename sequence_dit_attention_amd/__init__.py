@@ -7,6 +7,7 @@ from .api import (  # noqa: F401
     SP_BF16,
     SP_F32,
     exchange_sim,
+    qk_norm_rope,
     rope_apply,
     rope_apply_mx,
     shard_attn_fwd,

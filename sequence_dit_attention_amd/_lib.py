@@ -19,6 +19,8 @@ SIGNATURES = [
     ("rope_apply", ctypes.c_int, [_I32, _VP, _VP, _I64, _I32, _I32, _I64, ctypes.c_double, _I32, _VP]),
     ("rope_apply_mx", ctypes.c_int, [_I32, _VP, _VP, _I64, _I32, _I32, _VP, ctypes.POINTER(ctypes.c_int32),
                                      ctypes.c_double, _I32, _VP]),
+    ("qk_norm_rope", ctypes.c_int, [_I32, _VP, _VP, _I64, _I32, _I32, _VP, ctypes.c_double, _I64, _VP,
+                                    ctypes.POINTER(ctypes.c_int32), ctypes.c_double, _I32, _VP]),
     ("sp_av_positions", ctypes.c_int, [_I64, _I64, _I64, _I64, _I64, _I64, _PI64]),
     ("shard_attn_fwd", ctypes.c_int, [_I32, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I32, _I32,
                                       ctypes.c_float, _VP]),

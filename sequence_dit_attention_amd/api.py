@@ -124,6 +124,33 @@ def rope_apply_mx(x: torch.Tensor, pos: torch.Tensor, sections, theta: float = 1
     return y
 
 
+def qk_norm_rope(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6, pos0: int = 0,
+                 pos: torch.Tensor | None = None, sections=None, theta: float = 10000.0, style: str = "half",
+                 out: torch.Tensor | None = None) -> torch.Tensor:
+    """Per-head RMSNorm (weight gamma, float32 [d]) then RoPE of x [s, H, d]: 1-D positions pos0 + t when
+    pos is None, else multi-axis with pos (device int64 [s, 3]) and sections; in place when out is None."""
+    if x.dim() != 3:
+        raise ValueError("x must be [s, H, d]")
+    y = x if out is None else out
+    if y.shape != x.shape or y.dtype != x.dtype:
+        raise ValueError("out must match x in shape and dtype")
+    s, H, d = x.shape
+    if gamma.dtype != torch.float32 or tuple(gamma.shape) != (d,):
+        raise ValueError("gamma must be float32 [d]")
+    pp, sec = None, None
+    if pos is not None:
+        if pos.dtype != torch.int64 or tuple(pos.shape) != (s, 3):
+            raise ValueError("pos must be int64 [s, 3]")
+        if sections is None:
+            raise ValueError("sections are needed with pos")
+        pp = _dev(pos, "pos")
+        sec = (ctypes.c_int32 * 3)(*[int(v) for v in sections])
+    check("qk_norm_rope", lib().qk_norm_rope(_dtype_code(x), _dev(x, "x"), _dev(y, "out"), s, H, d,
+                                             _dev(gamma, "gamma"), float(eps), int(pos0), pp, sec, float(theta),
+                                             _STYLES[style], _stream(x)))
+    return y
+
+
 def sp_av_positions(T: int, Hh: int, Ww: int, n_audio: int, a: int, b: int) -> torch.Tensor:
     """Axis positions (host int64 tensor [b - a, 3]) of tokens [a, b) of a packed video + audio sequence."""
     outn = max(b - a, 0)

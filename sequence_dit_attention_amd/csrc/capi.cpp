@@ -270,6 +270,44 @@ int rope_apply_mx(int32_t dtype, const void* x, void* y, int64_t s, int32_t H, i
   return ok();
 }
 
+int qk_norm_rope(int32_t dtype, const void* x, void* y, int64_t s, int32_t H, int32_t d, const float* gamma,
+                 double eps, int64_t pos0, const int64_t* pos, const int32_t* sections, double theta, int32_t style,
+                 void* stream) {
+  const char* fn = "qk_norm_rope";
+  const int eb = elem_bytes(dtype);
+  if (!eb) return fail(SP_EINVAL, "%s: unknown dtype %d", fn, dtype);
+  if (style != SP_ROPE_HALF && style != SP_ROPE_INTERLEAVED) return fail(SP_EINVAL, "%s: unknown style %d", fn, style);
+  if (s < 0 || H < 1) return fail(SP_EINVAL, "%s: need s >= 0 and H >= 1", fn);
+  if (d < 2 || d > 1024 || (d & 1)) return fail(SP_EINVAL, "%s: d must be even, 2..1024 (got %d)", fn, d);
+  if (!spattn::norm_pairs_per_lane(d))
+    return fail(SP_EUNSUPPORTED, "%s: d = %d does not split into at most 64 lanes of 1, 2, 4 or 8 pairs", fn, d);
+  if (!(std::isfinite(theta) && theta > 0.0)) return fail(SP_EINVAL, "%s: theta must be finite and > 0", fn);
+  if (!(std::isfinite(eps) && eps >= 0.0 && eps <= 3.0e38)) return fail(SP_EINVAL, "%s: eps must be finite and >= 0", fn);
+  if (pos) {
+    if (!sections) return fail(SP_EINVAL, "%s: null sections with explicit positions", fn);
+    if (sections[0] < 0 || sections[1] < 0 || sections[2] < 0 || sections[0] + sections[1] + sections[2] != d / 2)
+      return fail(SP_EINVAL, "%s: sections must be >= 0 and add up to d/2 = %d pairs", fn, d / 2);
+  } else {
+    const int64_t lim = int64_t(1) << 53;
+    if (pos0 <= -lim || pos0 >= lim || pos0 + s >= lim)
+      return fail(SP_EINVAL, "%s: positions must stay within +-2^53", fn);
+  }
+  int64_t n, bytes, pbytes;
+  if (!mul_ok(s, int64_t(H) * d, &n) || !mul_ok(n, eb, &bytes) || !mul_ok(s, 3 * 8, &pbytes))
+    return fail(SP_ERANGE, "%s: size overflows int64", fn);
+  if (n == 0) return ok();
+  if (!x || !y || !gamma) return fail(SP_EINVAL, "%s: null device pointer", fn);
+  if (x != y && ranges_overlap(x, bytes, y, bytes)) return fail(SP_EOVERLAP, "%s: x and y overlap without being equal", fn);
+  if (ranges_overlap(gamma, int64_t(d) * 4, y, bytes)) return fail(SP_EOVERLAP, "%s: gamma overlaps y", fn);
+  if (pos && ranges_overlap(pos, pbytes, y, bytes)) return fail(SP_EOVERLAP, "%s: positions overlap y", fn);
+  const int sec[3] = {pos ? sections[0] : d / 2, pos ? sections[1] : 0, pos ? sections[2] : 0};
+  (void)hipGetLastError();
+  hipError_t e = spattn::launch_qk_norm_rope(dtype, x, y, s, H, d, gamma, static_cast<float>(eps), pos0, pos, sec,
+                                             theta, style, as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "qk_norm_rope launch");
+  return ok();
+}
+
 int sp_av_positions(int64_t T, int64_t Hh, int64_t Ww, int64_t n_audio, int64_t a, int64_t b, int64_t* out) {
   const char* fn = "sp_av_positions";
   if (T < 0 || Hh < 0 || Ww < 0 || n_audio < 0) return fail(SP_EINVAL, "%s: negative grid size", fn);

@@ -28,6 +28,13 @@ hipError_t launch_rope(int dtype, const void* x, void* y, int64_t s, int H, int 
 hipError_t launch_rope_mx(int dtype, const void* x, void* y, int64_t s, int H, int d, const int64_t* pos,
                           const int* sections, double theta, int style, hipStream_t stream);
 
+// Pairs per lane of the fused RMSNorm + RoPE kernel for head size d (the head
+// row must fit one wave: d/2 pairs in at most 64 lanes); 0 if unsupported.
+int norm_pairs_per_lane(int d);
+hipError_t launch_qk_norm_rope(int dtype, const void* x, void* y, int64_t s, int H, int d, const float* gamma,
+                               float eps, int64_t pos0, const int64_t* pos, const int* sections, double theta,
+                               int style, hipStream_t stream);
+
 // Attention of q[sq, H, d] against k, v[skv, H, d].
 hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                             int64_t sq, int64_t skv, int H, int d, float scale, hipStream_t stream);

@@ -10,6 +10,7 @@ from .gen import (  # noqa: F401
     f32_to_bf16_bits,
     bf16_bits_to_f32,
     gen_tensor,
+    gen_gamma,
     gen_qkv,
     sample_rows,
 )

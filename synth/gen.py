@@ -70,6 +70,13 @@ def gen_tensor(seed: int, tensor_id: int, S: int, H: int, d: int, dtype: str,
     return out
 
 
+def gen_gamma(seed: int, d: int) -> np.ndarray:
+    """A float32 RMSNorm weight [d]: 1 + 0.1 * N(0, 1), the spread of a trained
+    norm weight around its initial value of one (synthetic: no checkpoint)."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(entropy=seed, spawn_key=(7, d))))
+    return (1.0 + 0.1 * rng.standard_normal(d)).astype(np.float32)
+
+
 def gen_qkv(wl, scale_q: float = 1.0, threads: int | None = None):
     """Full [S, H, d] Q, K, V of a workload (see gen_tensor for the dtype).
 

@@ -28,7 +28,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert "shard_attn_fwd" in names and "shard_attn_fwd_gv" in names and len(names) == 11
+    assert "shard_attn_fwd" in names and "shard_attn_fwd_gv" in names and len(names) == 12
     h = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
         assert hasattr(h, n), n
@@ -123,6 +123,27 @@ def test_rope_mx_validation():
     assert f(1, FAKE, FAKE + 2, 10, 2, 8, FAKE * 2, sec, 1e4, 0, None) == SP_EOVERLAP    # partial x/y overlap
     assert f(1, FAKE, FAKE, 10, 2, 8, FAKE + 16, sec, 1e4, 0, None) == SP_EOVERLAP       # positions inside y
     assert f(1, FAKE, FAKE, 0, 2, 8, None, sec, 1e4, 0, None) == 0                        # s == 0: nothing to do
+
+
+def test_qk_norm_rope_validation():
+    L = _lib.lib()
+    f = L.qk_norm_rope
+    sec = (ctypes.c_int32 * 3)(2, 1, 1)
+    bad = (ctypes.c_int32 * 3)(2, 1, 2)
+    G = FAKE * 4  # a gamma address away from x and y
+    assert f(1, FAKE, FAKE, 10, 2, 8, G, -1e-6, 0, None, None, 1e4, 0, None) == SP_EINVAL        # eps < 0
+    assert f(1, FAKE, FAKE, 10, 2, 8, G, float("nan"), 0, None, None, 1e4, 0, None) == SP_EINVAL  # eps NaN
+    assert f(1, FAKE, FAKE, 10, 2, 8, None, 1e-6, 0, None, None, 1e4, 0, None) == SP_EINVAL      # null gamma
+    assert f(1, FAKE, FAKE, 10, 2, 130, G, 1e-6, 0, None, None, 1e4, 0, None) == SP_EUNSUPPORTED  # 65 pairs
+    assert f(1, FAKE, FAKE, 10, 2, 7, G, 1e-6, 0, None, None, 1e4, 0, None) == SP_EINVAL         # odd d
+    assert f(1, FAKE, FAKE, 10, 2, 8, G, 1e-6, 0, FAKE * 2, bad, 1e4, 0, None) == SP_EINVAL      # sections
+    assert f(1, FAKE, FAKE, 10, 2, 8, G, 1e-6, 0, FAKE * 2, None, 1e4, 0, None) == SP_EINVAL     # null sections
+    assert f(1, FAKE, FAKE, 10, 2, 8, G, 1e-6, 2**53, None, None, 1e4, 0, None) == SP_EINVAL     # 1-D positions
+    assert f(1, FAKE, FAKE + 2, 10, 2, 8, G, 1e-6, 0, None, None, 1e4, 0, None) == SP_EOVERLAP   # x / y
+    assert f(1, FAKE, FAKE, 10, 2, 8, FAKE + 8, 1e-6, 0, None, None, 1e4, 0, None) == SP_EOVERLAP  # gamma in y
+    assert f(1, FAKE, FAKE, 10, 2, 8, G, 1e-6, 0, FAKE + 16, sec, 1e4, 0, None) == SP_EOVERLAP   # pos in y
+    assert f(1, FAKE, FAKE, 10, 2, 8, G, 1e-6, 0, None, None, 1e4, 9, None) == SP_EINVAL         # style
+    assert f(1, FAKE, FAKE, 0, 2, 8, None, 1e-6, 0, None, None, 1e4, 0, None) == 0               # s == 0
 
 
 def test_av_positions_match_oracle():
