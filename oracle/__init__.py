@@ -19,6 +19,9 @@ from .spattn_oracle import (  # noqa: F401
     rope_apply,
     rope_apply_mx,
     av_positions,
+    tile_bounds,
+    tile_pack,
+    tile_unpack,
     rms_norm,
     qk_norm_rope,
     attention,

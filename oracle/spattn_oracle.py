@@ -21,6 +21,10 @@ Sources (page title, then section):
           (apply_rotary_pos_emb(query_states, key_states, cos, sin)).
         - section "消除FA中scale的冗余计算": the attention scale is 1/sqrt(d),
           computed once.
+        - section "VAE并行优化": a large image is cut along height and width
+          into blocks, one per process; attention inside the VAE gathers the
+          K and V of all blocks; at the end a two-stage gather puts every
+          block's result back at its spatial position in the full tensor.
 
 Readings where the pages are silent are listed in the design notes of the
 repository; the ones that shape the arithmetic here are: integer division is
@@ -227,6 +231,65 @@ def qk_norm_rope(x: np.ndarray, gamma: np.ndarray, eps: float, pos0: int = 0, po
     if pos is None:
         return rope_apply(xn, pos0, theta, style)
     return rope_apply_mx(xn, pos, sections, theta, style)
+
+
+# ---------------------------------------------------------------------------
+# 2-D spatial tiles of the VAE  [HY3, VAE并行优化]
+# ---------------------------------------------------------------------------
+
+
+def tile_bounds(Hh: int, Ww: int, pr: int, pc: int, p: int) -> tuple[int, int, int, int]:
+    """Block (r0, r1, c0, c1) of process p when an Hh x Ww grid is cut into pr x pc blocks.
+
+    [HY3, VAE并行优化] cuts the image along height and width into blocks, one
+    per process; how the cut falls is not stated.  Reading: processes are
+    numbered row-major over the block grid (p = i*pc + j) and each axis is cut
+    like the token ranges of [MH3, 机制一]: rows [Hh*i//pr, Hh*(i+1)//pr),
+    columns [Ww*j//pc, Ww*(j+1)//pc).
+    """
+    Hh, Ww, pr, pc, p = int(Hh), int(Ww), int(pr), int(pc), int(p)
+    if pr < 1 or pc < 1 or not (0 <= p < pr * pc) or Hh < 0 or Ww < 0:
+        raise ValueError("need pr, pc >= 1, 0 <= p < pr*pc, Hh, Ww >= 0")
+    i, j = divmod(p, pc)
+    r0, r1 = shard_bounds(Hh, pr, i)
+    c0, c1 = shard_bounds(Ww, pc, j)
+    return r0, r1, c0, c1
+
+
+def tile_pack(raster: np.ndarray, pr: int, pc: int) -> np.ndarray:
+    """Cut a channels-last raster [Hh, Ww, C] into its pr*pc blocks and lay them
+    out one after another in process order, each block row-major: [sum h_p*w_p, C].
+
+    This is the split of the input over the processes ([HY3, VAE并行优化], first
+    step) and, block after block, the AllGatherV receive buffer of the K and V
+    blocks ([MH3, 后端 A] with one block per process).
+    """
+    raster = np.asarray(raster)
+    Hh, Ww = raster.shape[0], raster.shape[1]
+    parts = []
+    for p in range(pr * pc):
+        r0, r1, c0, c1 = tile_bounds(Hh, Ww, pr, pc, p)
+        parts.append(raster[r0:r1, c0:c1].reshape((r1 - r0) * (c1 - c0), *raster.shape[2:]))
+    return np.concatenate(parts, axis=0)
+
+
+def tile_unpack(flat: np.ndarray, Hh: int, Ww: int, pr: int, pc: int) -> np.ndarray:
+    """Inverse of tile_pack: put each process's block back at its spatial position.
+
+    The second stage of the two-stage gather of [HY3, VAE并行优化] (the first
+    stage is the AllGatherV that concatenates the blocks in process order).
+    """
+    flat = np.asarray(flat)
+    out = np.zeros((Hh, Ww) + flat.shape[1:], dtype=flat.dtype)
+    a = 0
+    for p in range(pr * pc):
+        r0, r1, c0, c1 = tile_bounds(Hh, Ww, pr, pc, p)
+        n = (r1 - r0) * (c1 - c0)
+        out[r0:r1, c0:c1] = flat[a:a + n].reshape((r1 - r0), (c1 - c0), *flat.shape[1:])
+        a += n
+    if a != flat.shape[0]:
+        raise ValueError("flat does not hold exactly the pr*pc blocks")
+    return out
 
 
 def av_positions(T: int, Hh: int, Ww: int, n_audio: int, a: int, b: int) -> np.ndarray:
