@@ -167,6 +167,40 @@ int rope_apply_mx(int32_t dtype, const void* x, void* y, int64_t s, int32_t H, i
                   const int64_t* pos, const int32_t* sections, double theta, int32_t style, void* stream);
 
 /*
+ * sp_tile_bounds -- spatial block of process p in the VAE split (host).
+ * Page "NPU HunyuanImage-3.0模型推理优化实践", section VAE并行优化: a large image
+ * is cut along height and width into blocks, one per process.  Processes are
+ * numbered row-major over a pr x pc block grid (p = i*pc + j); each axis is
+ * cut like the token ranges of section 机制一:
+ *   out = {Hh*i/pr, Hh*(i+1)/pr, Ww*j/pc, Ww*(j+1)/pc}   (floor, exact)
+ * i.e. rows [out[0], out[1]) and columns [out[2], out[3]).
+ * Errors: SP_EINVAL (pr or pc < 1, p outside [0, pr*pc), negative sizes, null
+ * out), SP_ERANGE (pr*pc >= 2^31).  Host-only.
+ */
+int sp_tile_bounds(int64_t Hh, int64_t Ww, int32_t pr, int32_t pc, int32_t p, int64_t* out);
+
+/*
+ * tile_pack / tile_unpack -- between a raster and its blocks in process order.
+ * Section VAE并行优化 splits the input over the processes by its spatial
+ * dimensions and, at the end, gathers the blocks in two stages and puts each
+ * back at its original position.  With the blocks of sp_tile_bounds laid out
+ * one after another in process order, each row-major ([h_p, w_p, C]):
+ *   tile_pack:   flat  <- blocks of raster   (the split; also the order of
+ *                the AllGatherV receive buffer of the gathered K and V)
+ *   tile_unpack: raster <- blocks of flat    (second stage of the gather)
+ *   raster  device [Hh, Ww, C] of dtype, channels last
+ *   flat    device, at least Hh*Ww*C elements; block p starts at element
+ *           C * sum_{q<p} h_q*w_q
+ * Bit-exact copies.  Errors: SP_EINVAL (bad dtype, pr*pc outside [1, 65536],
+ * negative sizes, null pointers with data), SP_ERANGE (flat too small, size
+ * overflow), SP_EOVERLAP (raster and flat overlap), SP_EHIP.
+ */
+int tile_pack(int32_t dtype, const void* raster, int64_t Hh, int64_t Ww, int64_t C, int32_t pr, int32_t pc,
+              void* flat, int64_t flat_elems, void* stream);
+int tile_unpack(int32_t dtype, const void* flat, int64_t flat_elems, int64_t Hh, int64_t Ww, int64_t C, int32_t pr,
+                int32_t pc, void* raster, void* stream);
+
+/*
  * qk_norm_rope -- per-head RMSNorm of q or k fused with the rotary embedding.
  * Page "NPU HunyuanImage-3.0模型推理优化实践", section 计算分解: after the merged
  * QKV projection the query and key heads are normalised and then rotated
@@ -222,8 +256,12 @@ int sp_av_positions(int64_t T, int64_t Hh, int64_t Ww, int64_t n_audio, int64_t 
  * SP_F32: float32 throughout.  Each output row depends only on its own query
  * row and on K/V, in a fixed key order, so results are deterministic and a
  * row's result does not depend on sq or on where the row sits in q.
+ * Head sizes 64 and 128; SP_BF16 also 512 (the single-head attention over
+ * all channels of a VAE feature map, page "NPU HunyuanImage-3.0模型推理优化
+ * 实践", section VAE并行优化, where K and V of all spatial blocks are
+ * gathered).
  * Errors: SP_EINVAL (bad dtype, sq < 0, skv < 1, H < 1, scale not finite or
- * <= 0, null pointers with data), SP_EUNSUPPORTED (d not 64 or 128),
+ * <= 0, null pointers with data), SP_EUNSUPPORTED (other head sizes),
  * SP_ERANGE (sizes beyond the kernel's 32-bit grid, or 64 tokens of K spanning
  * 2 GiB or more), SP_EOVERLAP (o or lse
  * overlaps an input or each other), SP_EHIP.  sq == 0 enqueues nothing.
@@ -248,7 +286,8 @@ int shard_attn_fwd(int32_t dtype, const void* q, const void* k, const void* v,
  *   seq_lens   host array of W token counts (>= 0, sum >= 1)
  *   o, lse, sq, H, d, scale, stream  as in shard_attn_fwd
  * Errors: as shard_attn_fwd, plus SP_EINVAL (W < 1, null host arrays, a
- * negative length, a null shard with tokens), SP_EUNSUPPORTED (W > 16),
+ * negative length, a null shard with tokens), SP_EUNSUPPORTED (W > 16, or
+ * d = 512: head sizes 64 and 128 only),
  * SP_ERANGE (lengths overflow), SP_EOVERLAP (o or lse overlaps q, a shard or
  * each other).  sq == 0 enqueues nothing.
  */

@@ -16,6 +16,9 @@ from .api import (  # noqa: F401
     sp_allgatherv_layout,
     sp_av_positions,
     sp_shard_bounds,
+    sp_tile_bounds,
+    tile_pack,
+    tile_unpack,
     varlen_pack,
     varlen_unpack,
 )

@@ -21,6 +21,9 @@ SIGNATURES = [
                                      ctypes.c_double, _I32, _VP]),
     ("qk_norm_rope", ctypes.c_int, [_I32, _VP, _VP, _I64, _I32, _I32, _VP, ctypes.c_double, _I64, _VP,
                                     ctypes.POINTER(ctypes.c_int32), ctypes.c_double, _I32, _VP]),
+    ("sp_tile_bounds", ctypes.c_int, [_I64, _I64, _I32, _I32, _I32, _PI64]),
+    ("tile_pack", ctypes.c_int, [_I32, _VP, _I64, _I64, _I64, _I32, _I32, _VP, _I64, _VP]),
+    ("tile_unpack", ctypes.c_int, [_I32, _VP, _I64, _I64, _I64, _I64, _I32, _I32, _VP, _VP]),
     ("sp_av_positions", ctypes.c_int, [_I64, _I64, _I64, _I64, _I64, _I64, _PI64]),
     ("shard_attn_fwd", ctypes.c_int, [_I32, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I32, _I32,
                                       ctypes.c_float, _VP]),

@@ -151,6 +151,40 @@ def qk_norm_rope(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6, pos0: 
     return y
 
 
+def sp_tile_bounds(Hh: int, Ww: int, pr: int, pc: int, p: int) -> tuple[int, int, int, int]:
+    """Block (r0, r1, c0, c1) of process p when an Hh x Ww grid is cut into pr x pc blocks."""
+    out = (ctypes.c_int64 * 4)()
+    check("sp_tile_bounds", lib().sp_tile_bounds(Hh, Ww, pr, pc, p, out))
+    return out[0], out[1], out[2], out[3]
+
+
+def tile_pack(raster: torch.Tensor, pr: int, pc: int, flat: torch.Tensor | None = None) -> torch.Tensor:
+    """Blocks of raster [Hh, Ww, C] in process order, each row-major: flat [Hh*Ww, C] (or a given buffer)."""
+    if raster.dim() != 3:
+        raise ValueError("raster must be [Hh, Ww, C]")
+    Hh, Ww, C = raster.shape
+    if flat is None:
+        flat = torch.empty(Hh * Ww, C, dtype=raster.dtype, device=raster.device)
+    if flat.dtype != raster.dtype:
+        raise ValueError("flat must match raster's dtype")
+    check("tile_pack", lib().tile_pack(_dtype_code(raster), _dev(raster, "raster"), Hh, Ww, C, pr, pc,
+                                       _dev(flat, "flat"), flat.numel(), _stream(raster)))
+    return flat
+
+
+def tile_unpack(flat: torch.Tensor, Hh: int, Ww: int, pr: int, pc: int,
+                raster: torch.Tensor | None = None) -> torch.Tensor:
+    """Put the blocks of flat (process order, each row-major, C channels) back into raster [Hh, Ww, C]."""
+    C = flat.shape[-1]
+    if raster is None:
+        raster = torch.empty(Hh, Ww, C, dtype=flat.dtype, device=flat.device)
+    if raster.dtype != flat.dtype or tuple(raster.shape) != (Hh, Ww, C):
+        raise ValueError("raster must be [Hh, Ww, C] of flat's dtype")
+    check("tile_unpack", lib().tile_unpack(_dtype_code(flat), _dev(flat, "flat"), flat.numel(), Hh, Ww, C, pr, pc,
+                                           _dev(raster, "raster"), _stream(flat)))
+    return raster
+
+
 def sp_av_positions(T: int, Hh: int, Ww: int, n_audio: int, a: int, b: int) -> torch.Tensor:
     """Axis positions (host int64 tensor [b - a, 3]) of tokens [a, b) of a packed video + audio sequence."""
     outn = max(b - a, 0)

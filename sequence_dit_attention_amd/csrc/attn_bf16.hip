@@ -37,6 +37,12 @@
 //  * Work-groups are ordered head-major, so at any time all XCDs work on the
 //    same head: its K+V (188 MB at 367k tokens) stays in the 256 MB Infinity
 //    Cache and each XCD's L2 serves its co-resident query tiles.
+//  * Head size 512 (the single-head attention over the channels of a VAE
+//    feature map, page "NPU HunyuanImage-3.0模型推理优化实践", VAE并行优化):
+//    one 32-query block per wave (128 rows per work-group), 32-key tiles,
+//    and each work-group produces 256 of the 512 output columns, so a lane's
+//    O^T accumulators (128 registers) and Q fragments (128) fit; the two
+//    column halves are separate work-groups that both form the full scores.
 // Per output row the arithmetic depends only on that query row and on K/V in
 // a fixed key order, so results are deterministic and independent of sq and
 // of the row's position inside a tile.
@@ -67,8 +73,6 @@ typedef __attribute__((address_space(3))) void lds_void;
 #endif
 constexpr int kWaves = SPATTN_WAVES;   // waves per work-group
 constexpr int kThreads = 64 * kWaves;
-constexpr int QB = SPATTN_QB;          // 32-query MFMA blocks per wave
-constexpr int BM = kWaves * 32 * QB;   // query rows per work-group
 #ifndef SPATTN_RA
 #define SPATTN_RA 2  // LDS operand reads are issued this many MFMA groups ahead of their use
 #endif
@@ -80,33 +84,55 @@ constexpr int kLead = SPATTN_LEAD;     // K/V tiles in flight ahead of the tile 
 #ifndef SPATTN_BN
 #define SPATTN_BN 64
 #endif
-constexpr int kBN = SPATTN_BN;         // keys per tile
-constexpr int kSteps = kBN / 32;       // 32-key steps per tile
-static_assert(kSteps % 2 == 0, "the two S^T register sets alternate within a tile");
 constexpr int pow2_ceil(int x) { return x <= 1 ? 1 : 2 * pow2_ceil((x + 1) / 2); }
-// Slot counts are rounded up to powers of two (slot indices become masks)
-// when that still fits the 160 KiB of LDS.
-constexpr int slots(int n) { return (pow2_ceil(kLead + 2) + pow2_ceil(kLead + 1)) * kBN * 256 <= 160 * 1024
-                                        ? pow2_ceil(n) : n; }
-constexpr int kKSlots = slots(kLead + 2);  // K: tiles t, t+1 read, t+2 .. t+1+kLead loading
-constexpr int kVSlots = slots(kLead + 1);  // V: tile t read, t+1 .. t+kLead loading
 constexpr float kTau = 8.0f;           // lazy-rescale threshold (log2 units)
 constexpr float kLn2 = 0.69314718055994531f;
 
-template <int D>
+// Shape of the kernel for head size D.  D <= 128: two 32-query blocks per
+// wave (QB), 64-key tiles, every output column.  D = 512: a work-group
+// produces DV = 256 of the output columns (the O^T accumulator of a 32-query
+// block over all 512 would take every register a lane has), one query block
+// per wave, and 32-key tiles (64 keys x 1 KiB rows would not leave room for
+// the pipeline's slots in the 160 KiB of LDS).
+template <int D, int DV = D>
 struct Geo {
-  static constexpr int kCh = D / 8;                       // 16-byte chunks per K/V row
+  static constexpr int kD = D;
+  static constexpr int kDV = DV;
+  static constexpr int QB = D <= 128 ? SPATTN_QB : 1;     // 32-query MFMA blocks per wave
+  static constexpr int BM = kWaves * 32 * QB;             // query rows per work-group
+  static constexpr int kBN = D <= 128 ? SPATTN_BN : 32;   // keys per tile
+  static constexpr int kSteps = kBN / 32;                 // 32-key steps per tile
+  static_assert(kSteps == 1 || kSteps % 2 == 0, "the two S^T register sets alternate within a tile");
+  // With two or more steps per tile, the first K fragments of the block after
+  // next are read ahead at the end of a step; with one step that block is two
+  // tiles ahead and the fragments are read at the start of the step instead.
+  static constexpr bool kPrefetch = kSteps >= 2;
+  static constexpr int kCh = D / 8;                       // 16-byte chunks per K row
+  static constexpr int kVCh = DV / 8;                     // 16-byte chunks per V row (its DV columns)
   static constexpr int kDC = D / 16;                      // k-steps of the Q.K MFMA
-  static constexpr int kND = D / 32;                      // 32-row d-blocks of O^T
-  static constexpr int kRowB = D * 2;                     // bytes per K/V row
-  static constexpr int kTileB = kBN * kRowB;              // bytes per K or V tile
-  static constexpr int kLoads = kTileB / (kThreads * 16); // LDS-direct loads per lane per tile
+  static constexpr int kND = DV / 32;                     // 32-row d-blocks of O^T
+  static constexpr int kRowB = D * 2;                     // bytes per K row
+  static constexpr int kVRowB = DV * 2;                   // bytes per V row in LDS
+  static constexpr int kTileB = kBN * kRowB;              // bytes per K tile
+  static constexpr int kVTileB = kBN * kVRowB;            // bytes per V tile
+  static constexpr int kLoads = kTileB / (kThreads * 16); // LDS-direct loads per lane per K tile
+  static constexpr int kVLoads = kVTileB / (kThreads * 16);
+  // K: tile t+1 read (and tile t too when a tile holds several steps),
+  // t+2 .. t+1+kLead loading.  V: tile t read, t+1 .. t+kLead loading.  Slot
+  // counts are rounded up to powers of two (slot indices become masks) when
+  // that still fits the 160 KiB of LDS.
+  static constexpr int kKNeed = kLead + (kSteps >= 2 ? 2 : 1);
+  static constexpr int kVNeed = kLead + 1;
+  static constexpr bool kPow2 = pow2_ceil(kKNeed) * kTileB + pow2_ceil(kVNeed) * kVTileB <= 160 * 1024;
+  static constexpr int kKSlots = kPow2 ? pow2_ceil(kKNeed) : kKNeed;
+  static constexpr int kVSlots = kPow2 ? pow2_ceil(kVNeed) : kVNeed;
+  static_assert(kKSlots * kTileB + kVSlots * kVTileB <= 160 * 1024, "K/V slots exceed the LDS");
   // K rows: chunk c of row r lives at c ^ (r mod kCh): the 32 rows an MFMA
   // operand read touches land on distinct chunk columns.
   static __device__ int swz_k(int r) { return r & (kCh - 1); }
   // V rows: the transposing read takes 4 rows x 32 bytes per 16 lanes; XOR
-  // with 4*(r mod kCh/4) moves those rows to different 64-byte bank groups.
-  static __device__ int swz_v(int r) { return (r & (kCh / 4 - 1)) << 2; }
+  // with 4*(r mod kVCh/4) moves those rows to different 64-byte bank groups.
+  static __device__ int swz_v(int r) { return (r & (kVCh / 4 - 1)) << 2; }
 };
 
 __device__ inline float other_half_max(float x) {
@@ -129,18 +155,19 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
 // bytes [16i, 16i+16) of its block, so the per-lane source offsets (row, and
 // the chunk that the XOR swizzle maps to that position) are fixed for the
 // whole kernel and only the tile base (scalar) moves.
-template <int D, bool IS_V>
+template <typename G, bool IS_V>
 struct TileLoader {
-  using G = Geo<D>;
-  uint32_t voff[G::kLoads];  // byte offset of this lane's chunk from the tile's first row
-  int rows[G::kLoads];       // tile row this lane loads
+  static constexpr int kLoads = IS_V ? G::kVLoads : G::kLoads;
+  static constexpr int kRowB = IS_V ? G::kVRowB : G::kRowB;  // bytes of a tile row in LDS
+  uint32_t voff[kLoads];  // byte offset of this lane's chunk from the tile's first row
+  int rows[kLoads];       // tile row this lane loads
 
   __device__ void init(int wave, int lane, int64_t rowbytes) {
 #pragma unroll
-    for (int i = 0; i < G::kLoads; ++i) {
-      const int byte = (wave * G::kLoads + i) * 1024 + lane * 16;
-      const int r = byte / G::kRowB;
-      const int p = (byte % G::kRowB) >> 4;
+    for (int i = 0; i < kLoads; ++i) {
+      const int byte = (wave * kLoads + i) * 1024 + lane * 16;
+      const int r = byte / kRowB;
+      const int p = (byte % kRowB) >> 4;
       const int c = p ^ (IS_V ? G::swz_v(r) : G::swz_k(r));
       rows[i] = r;
       voff[i] = uint32_t(r * rowbytes + c * 16);
@@ -166,25 +193,25 @@ struct TileLoader {
   }
   // Full tile: every row < skv.
   __device__ void load(const uint16_t* hb, int tile, int64_t rowbytes, char* lds, int wave) const {
-    const char* base = reinterpret_cast<const char*>(hb) + int64_t(tile) * kBN * rowbytes;
+    const char* base = reinterpret_cast<const char*>(hb) + int64_t(tile) * G::kBN * rowbytes;
     const i32x4 rs = rsrc(base);
 #pragma unroll
-    for (int i = 0; i < G::kLoads; ++i) issue(rs, lds + (wave * G::kLoads + i) * 1024, voff[i]);
+    for (int i = 0; i < kLoads; ++i) issue(rs, lds + (wave * kLoads + i) * 1024, voff[i]);
   }
   // Full tile at byte address `addr` (wave-uniform).
   __device__ void load_at(uint64_t addr, char* lds, int wave) const {
     const i32x4 rs = rsrc(reinterpret_cast<const char*>(addr));
 #pragma unroll
-    for (int i = 0; i < G::kLoads; ++i) issue(rs, lds + (wave * G::kLoads + i) * 1024, voff[i]);
+    for (int i = 0; i < kLoads; ++i) issue(rs, lds + (wave * kLoads + i) * 1024, voff[i]);
   }
   // Tile whose first row is at `base` (wave-uniform); rows >= valid re-read
   // row valid-1 (see load_clamped).
   __device__ void load_base(const char* base, int valid, int64_t rowbytes, char* lds, int wave) const {
     const i32x4 rs = rsrc(base);
 #pragma unroll
-    for (int i = 0; i < G::kLoads; ++i) {
+    for (int i = 0; i < kLoads; ++i) {
       const int over = rows[i] >= valid ? rows[i] - (valid - 1) : 0;
-      issue(rs, lds + (wave * G::kLoads + i) * 1024, voff[i] - uint32_t(over * rowbytes));
+      issue(rs, lds + (wave * kLoads + i) * 1024, voff[i] - uint32_t(over * rowbytes));
     }
   }
   // Tile whose rows come from several shards: every lane finds the shard of
@@ -192,7 +219,7 @@ struct TileLoader {
   __device__ void load_gather(const KvShards& kv, const void* const* ptr, int64_t hoff, int key0, int keyL,
                               int64_t rowbytes, char* lds, int wave) const {
 #pragma unroll
-    for (int i = 0; i < G::kLoads; ++i) {
+    for (int i = 0; i < kLoads; ++i) {
       const int key = min(key0 + rows[i], keyL);
       int r = 0;
       for (int b = 1; b < kv.W; ++b) r += kv.start[b] <= key ? 1 : 0;
@@ -200,7 +227,7 @@ struct TileLoader {
       const uint64_t addr = reinterpret_cast<uint64_t>(ptr[r]) + uint64_t(hoff) +
                             uint64_t(key - kv.start[r]) * uint64_t(rowbytes) + chunk;
       const uint32_t m0 =
-          __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>(lds + (wave * G::kLoads + i) * 1024)));
+          __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>(lds + (wave * kLoads + i) * 1024)));
       asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(m0), "v"(addr) : "memory", "m0");
     }
   }
@@ -208,13 +235,13 @@ struct TileLoader {
   // those keys are masked to -inf, so they carry zero weight).
   __device__ void load_clamped(const uint16_t* hb, int tile, int skv, int64_t rowbytes, char* lds,
                                int wave) const {
-    const char* base = reinterpret_cast<const char*>(hb) + int64_t(tile) * kBN * rowbytes;
+    const char* base = reinterpret_cast<const char*>(hb) + int64_t(tile) * G::kBN * rowbytes;
     const i32x4 rs = rsrc(base);
-    const int valid = skv - tile * kBN;
+    const int valid = skv - tile * G::kBN;
 #pragma unroll
-    for (int i = 0; i < G::kLoads; ++i) {
+    for (int i = 0; i < kLoads; ++i) {
       const int over = rows[i] >= valid ? rows[i] - (valid - 1) : 0;
-      issue(rs, lds + (wave * G::kLoads + i) * 1024, voff[i] - uint32_t(over * rowbytes));
+      issue(rs, lds + (wave * kLoads + i) * 1024, voff[i] - uint32_t(over * rowbytes));
     }
   }
 };
@@ -222,7 +249,7 @@ struct TileLoader {
 // S^T of 32 keys (rows r0 .. r0+31 of an LDS K tile) against the wave's 64
 // queries.  MASKED: accumulated onto `init` (-inf on keys past the end of the
 // sequence, else 0); otherwise onto the inline constant 0.
-template <int D, bool MASKED>
+template <int D, bool MASKED, int QB = Geo<D>::QB>
 __device__ inline void qk32(f32x16 (&s)[QB], const char* kb, int r0, const bf16x8 (&qf)[QB][Geo<D>::kDC],
                             const f32x16& init, int col, int hf) {
   using G = Geo<D>;
@@ -252,7 +279,8 @@ __device__ inline f32x16 tail_init(int key0, int skv, int hf) {
   return m;
 }
 
-// Softmax state of the wave's 64 query columns (both wave halves hold the same values).
+// Softmax state of the wave's 32*QB query columns (both wave halves hold the same values).
+template <int QB>
 struct SoftState {
   float m_run[QB];  // reference maximum (log2 units) the probabilities are taken against
   float thr[QB];    // raw-score threshold (m_run + kTau) / c above which the reference is raised
@@ -276,7 +304,8 @@ __device__ inline float max3(float a, float b, float c) {
 // columns whose maximum really exceeds the reference by more than kTau
 // raised; every other column keeps its reference (alpha = 1 exactly), so a
 // row's arithmetic never depends on the other rows of the wave.
-__device__ inline void update_ref(const float (&mx)[QB], SoftState& st, float c) {
+template <int QB>
+__device__ inline void update_ref(const float (&mx)[QB], SoftState<QB>& st, float c) {
   bool need = false;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) need |= mx[qb] > st.thr[qb];
@@ -294,7 +323,8 @@ __device__ inline void update_ref(const float (&mx)[QB], SoftState& st, float c)
 }
 
 // Maximum of a 32-key block, then the reference update.
-__device__ inline void block_max(const f32x16 (&s)[QB], SoftState& st, float c) {
+template <int QB>
+__device__ inline void block_max(const f32x16 (&s)[QB], SoftState<QB>& st, float c) {
   float mx[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -310,12 +340,13 @@ __device__ inline void block_max(const f32x16 (&s)[QB], SoftState& st, float c) 
 // keys (8u + 2e, 8u + 2e + 1) of the lane's accumulator order; pw[qb][u][0..3]
 // is the B operand of P*V MFMA u.  (Kept as plain 32-bit words: element
 // extraction from a vector type under __builtin_bit_cast was miscompiled.)
-typedef uint32_t PW[QB][2][4];
+template <int QB>
+using PW = uint32_t[QB][2][4];
 
-template <int D>
-__device__ inline void rescale_o(f32x16 (&o)[Geo<D>::kND][QB], const float (&alpha)[QB]) {
+template <typename G, int QB = G::QB>
+__device__ inline void rescale_o(f32x16 (&o)[G::kND][QB], const float (&alpha)[QB]) {
 #pragma unroll
-  for (int db = 0; db < Geo<D>::kND; ++db)
+  for (int db = 0; db < G::kND; ++db)
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -349,19 +380,20 @@ __device__ inline void slot_items(int i, F&& f) {
     if (w * M / N == i) f(w);
 }
 
-template <int D, bool HAS_NEXT, bool MASK_NEXT, bool PRE_NEXT>
-__device__ __attribute__((always_inline)) inline void step32(f32x16 (&cur)[QB], f32x16 (&nxt)[QB], SoftState& st, PW& pb,
-                              f32x16 (&acc)[Geo<D>::kND][QB], const bf16x8 (&qf)[QB][Geo<D>::kDC],
+template <typename G, bool HAS_NEXT, bool MASK_NEXT, bool PRE_NEXT, int QB = G::QB>
+__device__ __attribute__((always_inline)) inline void step32(f32x16 (&cur)[QB], f32x16 (&nxt)[QB], SoftState<QB>& st,
+                              PW<QB>& pb,
+                              f32x16 (&acc)[G::kND][QB], const bf16x8 (&qf)[QB][G::kDC],
                               const char* kb_next, int rk_next, const f32x16& init_next, const char* vb, int rv,
                               float c, int lane, int col, int hf, bf16x8 (&kpre)[kRA], const char* kb_after,
                               int rk_after) {
-  using G = Geo<D>;
+  constexpr int D = G::kD;
   constexpr int kA = QB * G::kDC;      // MFMA slots of part A: S^T of the next block
   constexpr int kB = 2 * QB * G::kND;  // MFMA slots of part B: P*V
   constexpr int kNV = 2 * G::kND;      // V^T fragments (MFMA pairs u, db) per step
   static_assert(kA >= 2 * kRA && kB >= 2 * kRA, "prefetch slots");
   if (st.any) {  // reference raised at the end of the previous step
-    rescale_o<D>(acc, st.alpha);
+    rescale_o<G>(acc, st.alpha);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) st.l_run[qb] *= st.alpha[qb];
   }
@@ -374,8 +406,8 @@ __device__ __attribute__((always_inline)) inline void step32(f32x16 (&cur)[QB], 
     const int ra = rv + 16 * u + 4 * hf + (j16 >> 2);
     const int dcol = db * 32 + 16 * (g16 & 1) + 4 * (j16 & 3);
     const int ch = dcol >> 3, inb = (dcol & 7) * 2;
-    const char* p0 = vb + ra * G::kRowB + ((ch ^ G::swz_v(ra)) << 4) + inb;
-    const char* p1 = vb + (ra + 8) * G::kRowB + ((ch ^ G::swz_v(ra + 8)) << 4) + inb;
+    const char* p0 = vb + ra * G::kVRowB + ((ch ^ G::swz_v(ra)) << 4) + inb;
+    const char* p1 = vb + (ra + 8) * G::kVRowB + ((ch ^ G::swz_v(ra + 8)) << 4) + inb;
     const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
     const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p1);
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -400,7 +432,7 @@ __device__ __attribute__((always_inline)) inline void step32(f32x16 (&cur)[QB], 
   bf16x8 kf[G::kDC];
   if (HAS_NEXT) {
 #pragma unroll
-    for (int r = 0; r < kRA; ++r) kf[r] = kpre[r];
+    for (int r = 0; r < kRA; ++r) kf[r] = G::kPrefetch ? kpre[r] : kread(r);
   }
 #pragma unroll
   for (int i = 0; i < kA; ++i) {
@@ -490,20 +522,26 @@ struct KvFlat {
 template <bool GV>
 using KvArg = typename std::conditional<GV, KvShards, KvFlat>::type;
 
-template <int D, bool GV>
+template <int D, int DV, bool GV>
 __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const uint16_t* __restrict__ q, const KvArg<GV> kv,
                                                              uint16_t* __restrict__ o, float* __restrict__ lse,
                                                              int sq, int skv, int H, float c, int nqt) {
-  using G = Geo<D>;
+  using G = Geo<D, DV>;
+  constexpr int QB = G::QB, BM = G::BM, kBN = G::kBN, kSteps = G::kSteps;
+  constexpr int kKSlots = G::kKSlots, kVSlots = G::kVSlots;
+  constexpr int kNCB = D / DV;  // output column blocks per head
   // K tile j lives in slot j mod kKSlots, V tile j in slot j mod kVSlots.
-  __shared__ __attribute__((aligned(1024))) char smem[(kKSlots + kVSlots) * G::kTileB];
+  __shared__ __attribute__((aligned(1024))) char smem[kKSlots * G::kTileB + kVSlots * G::kVTileB];
   char* const vbase = smem + kKSlots * G::kTileB;
-  constexpr unsigned kBatch = 2 * G::kLoads;  // LDS-direct loads per wave per tile (K and V)
+  constexpr unsigned kBatch = G::kLoads + G::kVLoads;  // LDS-direct loads per wave per tile (K and V)
 
-  // Head-major order: consecutive work-groups (spread over all XCDs) share a head.
+  // Head-major order: consecutive work-groups (spread over all XCDs) share a
+  // head; within a head, column block cb of every query tile, then the next.
   const int L = blockIdx.x;
-  const int h = L / nqt;
-  const int qt = L - h * nqt;
+  const int hc = L / nqt;
+  const int qt = L - hc * nqt;
+  const int h = hc / kNCB;
+  const int cb = hc - h * kNCB;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -516,17 +554,17 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const uint16_t* __r
   const uint16_t* vh = nullptr;
   if constexpr (!GV) {
     kh = kv.k + int64_t(h) * D;
-    vh = kv.v + int64_t(h) * D;
+    vh = kv.v + int64_t(h) * D + cb * DV;
   }
   const int nT = (skv + kBN - 1) / kBN;
   const bool ragged = (skv % kBN) != 0;
 
-  TileLoader<D, false> kl;
-  TileLoader<D, true> vl;
+  TileLoader<G, false> kl;
+  TileLoader<G, true> vl;
   kl.init(wave, lane, rowbytes);
   vl.init(wave, lane, rowbytes);
   auto kslot = [&](int j) { return smem + (j % kKSlots) * G::kTileB; };
-  auto vslot = [&](int j) { return vbase + (j % kVSlots) * G::kTileB; };
+  auto vslot = [&](int j) { return vbase + (j % kVSlots) * G::kVTileB; };
   // Tile indices past the end are clamped: those loads land in slots no live
   // tile uses and keep every batch the same size for the vmcnt accounting.
   // Sharded K/V: a cursor per stream (K, V) follows the shard that holds the
@@ -537,13 +575,14 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const uint16_t* __r
   struct Cursor {
     int r;           // shard holding the last tile's first key
     int s0, s1;      // its token range [s0, s1)
-    const char* p;   // its base pointer, offset to head h
+    const char* p;   // its base pointer, offset to the stream's columns of head h
+    int64_t off;     // that byte offset inside a token row
   };
-  const int64_t hoff = int64_t(h) * D * 2;
-  Cursor kcur{0, 0, 0, nullptr}, vcur{0, 0, 0, nullptr};
+  const int64_t hoff = int64_t(h) * D * 2, hoff_v = hoff + int64_t(cb) * DV * 2;
+  Cursor kcur{0, 0, 0, nullptr, 0}, vcur{0, 0, 0, nullptr, 0};
   if constexpr (GV) {
-    kcur = Cursor{0, 0, int(kv.start[1]), static_cast<const char*>(kv.k[0]) + hoff};
-    vcur = Cursor{0, 0, int(kv.start[1]), static_cast<const char*>(kv.v[0]) + hoff};
+    kcur = Cursor{0, 0, int(kv.start[1]), static_cast<const char*>(kv.k[0]) + hoff, hoff};
+    vcur = Cursor{0, 0, int(kv.start[1]), static_cast<const char*>(kv.v[0]) + hoff_v, hoff_v};
   }
   auto load_sharded = [&](const auto& ld, const void* const* ptr, Cursor& cu, int tile, char* lds) {
     if constexpr (GV) {
@@ -553,14 +592,14 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const uint16_t* __r
         ++cu.r;
         cu.s0 = cu.s1;
         cu.s1 = int(kv.start[cu.r + 1]);
-        cu.p = static_cast<const char*>(ptr[cu.r]) + hoff;
+        cu.p = static_cast<const char*>(ptr[cu.r]) + cu.off;
       }
       if (keyL < cu.s1) {
         const char* base = cu.p + int64_t(key0 - cu.s0) * rowbytes;
         if (keyL - key0 + 1 == kBN) ld.load_at(reinterpret_cast<uint64_t>(base), lds, wave);
         else ld.load_base(base, keyL - key0 + 1, rowbytes, lds, wave);
       } else {
-        ld.load_gather(kv, ptr, hoff, key0, keyL, rowbytes, lds, wave);
+        ld.load_gather(kv, ptr, cu.off, key0, keyL, rowbytes, lds, wave);
       }
     }
   };
@@ -606,7 +645,7 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const uint16_t* __r
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[db][qb][r] = 0.f;
-  SoftState st;
+  SoftState<QB> st;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     st.m_run[qb] = -INFINITY;
@@ -617,7 +656,7 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const uint16_t* __r
   const f32x16 zero = {};
 
   f32x16 sa[QB], sb[QB];  // S^T of the current / next 32 keys
-  PW pb;
+  PW<QB> pb;
 
   tile_barrier<0>();
   if (nT == 1) qk32<D, true>(sa, kslot(0), 0, qf, tail_init(0, skv, hf), col, hf);
@@ -626,8 +665,10 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const uint16_t* __r
   // K fragments of the next step's part A are read ahead, at the end of the
   // previous part B (that K tile has been resident since an earlier barrier).
   bf16x8 kpre[kRA];
+  if constexpr (G::kPrefetch) {
 #pragma unroll
-  for (int r = 0; r < kRA; ++r) kpre[r] = k_frag<D>(kslot(0), 32, r, col, hf);
+    for (int r = 0; r < kRA; ++r) kpre[r] = k_frag<D>(kslot(0), 32, r, col, hf);
+  }
   // Tile t (kBN keys) = kSteps 32-key steps.  At its top batch t (K t+1, V t)
   // has landed, batches t+1 .. t+kLead-1 may still be in flight, and batch
   // t+kLead is issued into the slots that tile t-1 released.
@@ -646,18 +687,22 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const uint16_t* __r
       constexpr bool next_in = s + 1 < kSteps, after_in = s + 2 < kSteps;
       constexpr bool HAS_NEXT = next_in || !LAST;
       constexpr bool MASK_NEXT = next_in ? LAST : NEXT_LAST;
-      constexpr bool PRE_NEXT = after_in || !LAST;
+      constexpr bool PRE_NEXT = G::kPrefetch && (after_in || !LAST);
       const char* kb_next = next_in ? kc : kn;
       const char* kb_after = after_in ? kc : kn;
       const int rk_next = next_in ? 32 * (s + 1) : 0;
       const int rk_after = after_in ? 32 * (s + 2) : 32 * (s + 2 - kSteps);
       const f32x16 init = MASK_NEXT ? tail_init(t * kBN + 32 * (s + 1), skv, hf) : zero;
       if constexpr (s % 2 == 0)
-        step32<D, HAS_NEXT, MASK_NEXT, PRE_NEXT>(sa, sb, st, pb, acc, qf, kb_next, rk_next, init, vb, 32 * s, c,
+        step32<G, HAS_NEXT, MASK_NEXT, PRE_NEXT>(sa, sb, st, pb, acc, qf, kb_next, rk_next, init, vb, 32 * s, c,
                                                  lane, col, hf, kpre, kb_after, rk_after);
       else
-        step32<D, HAS_NEXT, MASK_NEXT, PRE_NEXT>(sb, sa, st, pb, acc, qf, kb_next, rk_next, init, vb, 32 * s, c,
+        step32<G, HAS_NEXT, MASK_NEXT, PRE_NEXT>(sb, sa, st, pb, acc, qf, kb_next, rk_next, init, vb, 32 * s, c,
                                                  lane, col, hf, kpre, kb_after, rk_after);
+      if constexpr (kSteps == 1) {  // one step per tile: the next tile's S^T moves to the current set
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) sa[qb] = sb[qb];
+      }
     };
     for_each_index(std::make_integer_sequence<int, kSteps>{}, one);
   };
@@ -707,7 +752,7 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const uint16_t* __r
     const float inv = 1.f / lt;
     const int row = qrow0 + qb * 32 + col;
     if (row < sq) {
-      uint16_t* dst = o + int64_t(row) * rowstride + int64_t(h) * D;
+      uint16_t* dst = o + int64_t(row) * rowstride + int64_t(h) * D + cb * DV;
 #pragma unroll
       for (int db = 0; db < G::kND; ++db)
 #pragma unroll
@@ -718,18 +763,18 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const uint16_t* __r
           w[1] = pack_bf16x2(acc[db][qb][4 * g + 2] * inv, acc[db][qb][4 * g + 3] * inv);
           *reinterpret_cast<u32x2*>(dst + d0) = w;
         }
-      if (lse && hf == 0) lse[int64_t(h) * sq + row] = (st.m_run[qb] + __log2f(lt)) * kLn2;
+      if (lse && hf == 0 && cb == 0) lse[int64_t(h) * sq + row] = (st.m_run[qb] + __log2f(lt)) * kLn2;
     }
   }
 }
 
-template <int D, bool GV>
+template <int D, int DV, bool GV>
 hipError_t launch_d(const void* q, const KvArg<GV>& kv, void* o, float* lse, int64_t sq, int64_t skv, int H,
                     float c, hipStream_t stream) {
-  const int64_t nqt = (sq + BM - 1) / BM;
-  const int64_t grid = nqt * H;
+  const int64_t nqt = (sq + Geo<D, DV>::BM - 1) / Geo<D, DV>::BM;
+  const int64_t grid = nqt * H * (D / DV);
   if (grid > kMaxGrid) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((attn_bf16_kernel<D, GV>), dim3(unsigned(grid)), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((attn_bf16_kernel<D, DV, GV>), dim3(unsigned(grid)), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(q), kv, static_cast<uint16_t*>(o), lse, int(sq), int(skv), H, c,
                      int(nqt));
   return hipGetLastError();
@@ -742,8 +787,9 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o
   if (sq > (int64_t(1) << 31) - 1024) return hipErrorInvalidValue;
   const float c = scale * 1.4426950408889634f;
   const KvFlat kv{static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v)};
-  if (d == 64) return launch_d<64, false>(q, kv, o, lse, sq, skv, H, c, stream);
-  return launch_d<128, false>(q, kv, o, lse, sq, skv, H, c, stream);
+  if (d == 64) return launch_d<64, 64, false>(q, kv, o, lse, sq, skv, H, c, stream);
+  if (d == 512) return launch_d<512, 256, false>(q, kv, o, lse, sq, skv, H, c, stream);
+  return launch_d<128, 128, false>(q, kv, o, lse, sq, skv, H, c, stream);
 }
 
 hipError_t launch_attn_bf16_gv(const void* q, const KvShards& kv, void* o, float* lse, int64_t sq, int H, int d,
@@ -751,8 +797,8 @@ hipError_t launch_attn_bf16_gv(const void* q, const KvShards& kv, void* o, float
   if (sq > (int64_t(1) << 31) - 1024) return hipErrorInvalidValue;
   const float c = scale * 1.4426950408889634f;
   const int64_t skv = kv.start[kv.W];
-  if (d == 64) return launch_d<64, true>(q, kv, o, lse, sq, skv, H, c, stream);
-  return launch_d<128, true>(q, kv, o, lse, sq, skv, H, c, stream);
+  if (d == 64) return launch_d<64, 64, true>(q, kv, o, lse, sq, skv, H, c, stream);
+  return launch_d<128, 128, true>(q, kv, o, lse, sq, skv, H, c, stream);
 }
 
 }  // namespace spattn

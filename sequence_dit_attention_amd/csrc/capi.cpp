@@ -81,11 +81,14 @@ namespace {
 // Checks shared by both attention entry points; fills the byte sizes of q/o,
 // of all K (or V) tokens, and of lse.
 int check_attn(const char* fn, int32_t dtype, int64_t sq, int64_t skv, int32_t H, int32_t d, float scale,
-               int64_t* qb, int64_t* kb, int64_t* lb) {
+               bool allow512, int64_t* qb, int64_t* kb, int64_t* lb) {
   const int eb = elem_bytes(dtype);
   if (!eb) return fail(SP_EINVAL, "%s: unknown dtype %d", fn, dtype);
   if (sq < 0 || skv < 1 || H < 1) return fail(SP_EINVAL, "%s: need sq >= 0, skv >= 1, H >= 1", fn);
-  if (d != 64 && d != 128) return fail(SP_EUNSUPPORTED, "%s: head size %d not supported (64, 128)", fn, d);
+  const bool d512 = allow512 && dtype == SP_BF16 && d == 512;
+  if (d != 64 && d != 128 && !d512)
+    return fail(SP_EUNSUPPORTED, "%s: head size %d not supported (64, 128%s)", fn, d,
+                allow512 ? "; 512 with bf16" : "");
   if (!(std::isfinite(scale) && scale > 0.f)) return fail(SP_EINVAL, "%s: scale must be finite and > 0", fn);
   int64_t qn, kn;
   if (!mul_ok(sq, int64_t(H) * d, &qn) || !mul_ok(skv, int64_t(H) * d, &kn) || !mul_ok(qn, eb, qb) ||
@@ -270,6 +273,79 @@ int rope_apply_mx(int32_t dtype, const void* x, void* y, int64_t s, int32_t H, i
   return ok();
 }
 
+int sp_tile_bounds(int64_t Hh, int64_t Ww, int32_t pr, int32_t pc, int32_t p, int64_t* out) {
+  const char* fn = "sp_tile_bounds";
+  if (!out) return fail(SP_EINVAL, "%s: null output", fn);
+  if (pr < 1 || pc < 1) return fail(SP_EINVAL, "%s: need pr, pc >= 1", fn);
+  if (int64_t(pr) * pc > (int64_t(1) << 31) - 1) return fail(SP_ERANGE, "%s: pr*pc too large", fn);
+  if (p < 0 || int64_t(p) >= int64_t(pr) * pc) return fail(SP_EINVAL, "%s: block %d outside [0, pr*pc)", fn, p);
+  if (Hh < 0 || Ww < 0) return fail(SP_EINVAL, "%s: negative grid size", fn);
+  const int32_t i = p / pc, j = p % pc;
+  const __int128 h = Hh, w = Ww;
+  out[0] = static_cast<int64_t>((h * i) / pr);
+  out[1] = static_cast<int64_t>((h * (i + 1)) / pr);
+  out[2] = static_cast<int64_t>((w * j) / pc);
+  out[3] = static_cast<int64_t>((w * (j + 1)) / pc);
+  return ok();
+}
+
+namespace {
+
+// Copies between a channels-last raster [Hh, Ww, C] and its pr*pc blocks laid
+// out one after another in block order (each block row-major).  One segment
+// per block, one outer step per block row: blocks of one block row share
+// their height, so each block row is one batch of copies.
+int tile_copy(const char* fn, bool to_flat, int32_t dtype, const void* raster, void* raster_out, int64_t Hh,
+              int64_t Ww, int64_t C, int32_t pr, int32_t pc, const void* flat_in, void* flat_out,
+              int64_t flat_elems, void* stream) {
+  const int eb = elem_bytes(dtype);
+  if (!eb) return fail(SP_EINVAL, "%s: unknown dtype %d", fn, dtype);
+  if (pr < 1 || pc < 1 || int64_t(pr) * pc > 65536) return fail(SP_EINVAL, "%s: need 1 <= pr*pc <= 65536", fn);
+  if (Hh < 0 || Ww < 0 || C < 0 || flat_elems < 0) return fail(SP_EINVAL, "%s: negative size", fn);
+  int64_t n, bytes;
+  if (!mul_ok(Hh, Ww, &n) || !mul_ok(n, C, &n) || !mul_ok(n, eb, &bytes))
+    return fail(SP_ERANGE, "%s: size overflows int64", fn);
+  if (flat_elems < n) return fail(SP_ERANGE, "%s: flat holds %lld elements, the blocks need %lld", fn,
+                                  (long long)flat_elems, (long long)n);
+  if (n == 0) return ok();
+  const void* rp = to_flat ? raster : raster_out;
+  const void* fp = to_flat ? static_cast<const void*>(flat_out) : flat_in;
+  if (!rp || !fp) return fail(SP_EINVAL, "%s: null device pointer", fn);
+  if (ranges_overlap(rp, bytes, fp, bytes)) return fail(SP_EOVERLAP, "%s: raster and flat overlap", fn);
+  const int64_t rowpitch = Ww * C * eb;  // bytes per raster row
+  int64_t off = 0;                       // element offset of the current block in flat
+  for (int32_t i = 0; i < pr; ++i) {
+    const __int128 h = Hh, w = Ww;
+    const int64_t r0 = static_cast<int64_t>((h * i) / pr), r1 = static_cast<int64_t>((h * (i + 1)) / pr);
+    std::vector<CopySeg> segs;
+    for (int32_t j = 0; j < pc; ++j) {
+      const int64_t c0 = static_cast<int64_t>((w * j) / pc), c1 = static_cast<int64_t>((w * (j + 1)) / pc);
+      const int64_t bw = (c1 - c0) * C * eb;  // bytes per block row
+      char* fl = static_cast<char*>(const_cast<void*>(fp)) + off * eb;
+      char* ra = static_cast<char*>(const_cast<void*>(rp)) + r0 * rowpitch + c0 * C * eb;
+      if (to_flat) segs.push_back(CopySeg{ra, fl, bw, rowpitch, bw});
+      else segs.push_back(CopySeg{fl, ra, bw, bw, rowpitch});
+      off += (r1 - r0) * (c1 - c0) * C;
+    }
+    const int rc = launch_copies(segs, r1 - r0, stream);
+    if (rc != SP_OK) return rc;
+  }
+  return ok();
+}
+
+}  // namespace
+
+int tile_pack(int32_t dtype, const void* raster, int64_t Hh, int64_t Ww, int64_t C, int32_t pr, int32_t pc,
+              void* flat, int64_t flat_elems, void* stream) {
+  return tile_copy("tile_pack", true, dtype, raster, nullptr, Hh, Ww, C, pr, pc, nullptr, flat, flat_elems, stream);
+}
+
+int tile_unpack(int32_t dtype, const void* flat, int64_t flat_elems, int64_t Hh, int64_t Ww, int64_t C, int32_t pr,
+                int32_t pc, void* raster, void* stream) {
+  return tile_copy("tile_unpack", false, dtype, nullptr, raster, Hh, Ww, C, pr, pc, flat, nullptr, flat_elems,
+                   stream);
+}
+
 int qk_norm_rope(int32_t dtype, const void* x, void* y, int64_t s, int32_t H, int32_t d, const float* gamma,
                  double eps, int64_t pos0, const int64_t* pos, const int32_t* sections, double theta, int32_t style,
                  void* stream) {
@@ -337,7 +413,7 @@ int sp_av_positions(int64_t T, int64_t Hh, int64_t Ww, int64_t n_audio, int64_t 
 int shard_attn_fwd(int32_t dtype, const void* q, const void* k, const void* v, void* o, float* lse,
                    int64_t sq, int64_t skv, int32_t H, int32_t d, float scale, void* stream) {
   int64_t qb, kb, lb;
-  if (int rc = check_attn("shard_attn_fwd", dtype, sq, skv, H, d, scale, &qb, &kb, &lb)) return rc;
+  if (int rc = check_attn("shard_attn_fwd", dtype, sq, skv, H, d, scale, true, &qb, &kb, &lb)) return rc;
   if (sq == 0) return ok();
   if (!q || !k || !v || !o) return fail(SP_EINVAL, "shard_attn_fwd: null device pointer");
   if (ranges_overlap(o, qb, q, qb) || ranges_overlap(o, qb, k, kb) || ranges_overlap(o, qb, v, kb))
@@ -375,7 +451,7 @@ int shard_attn_fwd_gv(int32_t dtype, const void* q, int32_t W, const void* const
   }
   const int64_t skv = kv.start[W];
   int64_t qb, kb, lb;
-  if (int rc = check_attn(fn, dtype, sq, skv, H, d, scale, &qb, &kb, &lb)) return rc;
+  if (int rc = check_attn(fn, dtype, sq, skv, H, d, scale, false, &qb, &kb, &lb)) return rc;
   if (sq == 0) return ok();
   if (!q || !o) return fail(SP_EINVAL, "%s: null device pointer", fn);
   const int64_t tok_bytes = int64_t(H) * d * elem_bytes(dtype);

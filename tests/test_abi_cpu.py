@@ -28,7 +28,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert "shard_attn_fwd" in names and "shard_attn_fwd_gv" in names and len(names) == 12
+    assert "shard_attn_fwd" in names and "shard_attn_fwd_gv" in names and len(names) == 15
     h = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
         assert hasattr(h, n), n
@@ -144,6 +144,28 @@ def test_qk_norm_rope_validation():
     assert f(1, FAKE, FAKE, 10, 2, 8, G, 1e-6, 0, FAKE + 16, sec, 1e4, 0, None) == SP_EOVERLAP   # pos in y
     assert f(1, FAKE, FAKE, 10, 2, 8, G, 1e-6, 0, None, None, 1e4, 9, None) == SP_EINVAL         # style
     assert f(1, FAKE, FAKE, 0, 2, 8, None, 1e-6, 0, None, None, 1e4, 0, None) == 0               # s == 0
+
+
+def test_tile_bounds_match_oracle_and_validation():
+    for Hh, Ww, pr, pc in [(7, 5, 2, 3), (128, 128, 2, 2), (84, 48, 3, 3), (0, 9, 2, 2), (5, 3, 7, 1),
+                           (2**40 + 3, 2**35 + 1, 5, 7)]:
+        for p in range(pr * pc):
+            assert api.sp_tile_bounds(Hh, Ww, pr, pc, p) == oracle.tile_bounds(Hh, Ww, pr, pc, p)
+    L = _lib.lib()
+    out = (ctypes.c_int64 * 4)()
+    assert L.sp_tile_bounds(4, 4, 2, 2, 4, out) == SP_EINVAL
+    assert L.sp_tile_bounds(4, 4, 0, 2, 0, out) == SP_EINVAL
+    assert L.sp_tile_bounds(-1, 4, 2, 2, 0, out) == SP_EINVAL
+    assert L.sp_tile_bounds(4, 4, 2, 2, 0, None) == SP_EINVAL
+    f, g = L.tile_pack, L.tile_unpack
+    assert f(1, FAKE, 4, 4, 8, 2, 2, FAKE * 2, 127, None) == SP_ERANGE      # flat too small
+    assert f(1, FAKE, 4, 4, 8, 2, 2, FAKE + 64, 128, None) == SP_EOVERLAP    # raster overlaps flat
+    assert f(7, FAKE, 4, 4, 8, 2, 2, FAKE * 2, 128, None) == SP_EINVAL      # dtype
+    assert f(1, FAKE, 4, 4, 8, 0, 2, FAKE * 2, 128, None) == SP_EINVAL      # pr
+    assert f(1, None, 4, 4, 8, 2, 2, FAKE * 2, 128, None) == SP_EINVAL      # null raster
+    assert g(1, FAKE * 2, 128, 4, 4, 8, 2, 2, None, None) == SP_EINVAL      # null raster
+    assert g(1, FAKE * 2, 100, 4, 4, 8, 2, 2, FAKE, None) == SP_ERANGE
+    assert g(1, FAKE * 2, 0, 0, 4, 8, 2, 2, None, None) == 0                # nothing to do
 
 
 def test_av_positions_match_oracle():
