@@ -271,6 +271,40 @@ int shard_attn_fwd(int32_t dtype, const void* q, const void* k, const void* v,
                    float scale, void* stream);
 
 /*
+ * shard_attn_fwd_split -- shard_attn_fwd with the keys cut into nsplit ranges
+ * that run as separate work-groups, for calls with too few query tiles to
+ * fill the GPU (the single-head attention of the VAE block split, page "NPU
+ * HunyuanImage-3.0模型推理优化实践", section VAE并行优化, has one head and a
+ * few thousand queries per process).  Range s covers whole key tiles
+ * [T*s/nsplit, T*(s+1)/nsplit) of the T tiles; each range yields its own
+ * normalised float32 output O_s and log-sum-exp L_s, and the results are
+ * combined exactly as the softmax over the union of the ranges:
+ *   O = sum_s exp(L_s - M) O_s / sum_s exp(L_s - M),  LSE = M + log sum_s exp(L_s - M)
+ * with M = max_s L_s, in float32, O rounded once to bf16.  With nsplit = 1
+ * the result is bit-identical to shard_attn_fwd.
+ *   q, k, v, o, lse, sq, skv, H, d, scale, stream  as in shard_attn_fwd
+ *                (SP_BF16 only; d 64, 128 or 512)
+ *   nsplit      1 .. min(1024, ceil(skv / 64))
+ *   workspace   device scratch of at least sp_attn_split_workspace(sq, H, d,
+ *               nsplit) bytes, 256-byte aligned, caller-owned; its contents
+ *               on entry do not matter and are overwritten
+ * Errors: as shard_attn_fwd, plus SP_EUNSUPPORTED (SP_F32), SP_EINVAL (nsplit
+ * out of range, null or misaligned workspace), SP_ERANGE (workspace too
+ * small), SP_EOVERLAP (workspace overlaps another buffer).
+ */
+int shard_attn_fwd_split(int32_t dtype, const void* q, const void* k, const void* v, void* o, float* lse,
+                         int64_t sq, int64_t skv, int32_t H, int32_t d, float scale, int32_t nsplit,
+                         void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * sp_attn_split_workspace -- bytes of workspace shard_attn_fwd_split needs:
+ * nsplit*sq*H*d float32 partial outputs (rounded up to 256 bytes) followed by
+ * nsplit*H*sq float32 partial log-sum-exps.  Negative status on bad
+ * arguments (SP_EINVAL) or overflow (SP_ERANGE).  Host-only.
+ */
+int64_t sp_attn_split_workspace(int64_t sq, int32_t H, int32_t d, int32_t nsplit);
+
+/*
  * shard_attn_fwd_gv -- shard_attn_fwd against K/V left in the W per-rank
  * shards, without the gather into one buffer.  Section 后端 A reassembles
  * the full sequence by concatenating the ranks' blocks in rank order; here

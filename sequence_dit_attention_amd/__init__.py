@@ -12,6 +12,8 @@ from .api import (  # noqa: F401
     rope_apply_mx,
     shard_attn_fwd,
     shard_attn_fwd_gv,
+    shard_attn_fwd_split,
+    split_workspace_bytes,
     sp_abi_version,
     sp_allgatherv_layout,
     sp_av_positions,

@@ -219,6 +219,46 @@ def shard_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch
     return out
 
 
+def split_workspace_bytes(sq: int, H: int, d: int, nsplit: int) -> int:
+    """Bytes of device workspace shard_attn_fwd_split needs."""
+    n = lib().sp_attn_split_workspace(sq, H, d, nsplit)
+    if n < 0:
+        check("sp_attn_split_workspace", int(n))
+    return int(n)
+
+
+def shard_attn_fwd_split(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, nsplit: int,
+                         out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                         scale: float | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """shard_attn_fwd with the keys cut into nsplit ranges (bf16); workspace: a device uint8 buffer of at
+    least split_workspace_bytes(...) bytes (allocated here with torch when None)."""
+    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape or q.shape[1:] != k.shape[1:]:
+        raise ValueError("q [sq,H,d], k and v [skv,H,d] with matching H, d")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v dtypes differ")
+    sq, H, d = q.shape
+    skv = k.shape[0]
+    if out is None:
+        out = torch.empty_like(q)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    lp = None
+    if lse is not None:
+        if lse.dtype != torch.float32 or lse.shape != (H, sq):
+            raise ValueError("lse must be float32 [H, sq]")
+        lp = _dev(lse, "lse")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = split_workspace_bytes(sq, H, d, nsplit)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    check("shard_attn_fwd_split", lib().shard_attn_fwd_split(
+        _dtype_code(q), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"), lp, sq, skv, H, d,
+        float(scale), int(nsplit), _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(q)))
+    return out
+
+
 def exchange_sim(shards, cat_dim: int = 0):
     """Single-GPU stand-in for exchange(rank, tensors, cat_dims): AllGatherV of
     per-rank shards (list of tensors equal except along cat_dim) through a flat

@@ -59,6 +59,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -522,10 +523,15 @@ struct KvFlat {
 template <bool GV>
 using KvArg = typename std::conditional<GV, KvShards, KvFlat>::type;
 
-template <int D, int DV, bool GV>
+// SPLIT: the keys are cut into nsplit ranges of whole tiles, one per
+// work-group index; each work-group writes its float32 O normalised over its
+// own keys and that range's LSE (opart [nsplit, sq, H, D], lse [nsplit, H, sq])
+// for merge_kernel to combine.
+template <int D, int DV, bool GV, bool SPLIT>
 __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const uint16_t* __restrict__ q, const KvArg<GV> kv,
                                                              uint16_t* __restrict__ o, float* __restrict__ lse,
-                                                             int sq, int skv, int H, float c, int nqt) {
+                                                             int sq, int skv_all, int H, float c, int nqt,
+                                                             int nsplit, float* __restrict__ opart) {
   using G = Geo<D, DV>;
   constexpr int QB = G::QB, BM = G::BM, kBN = G::kBN, kSteps = G::kSteps;
   constexpr int kKSlots = G::kKSlots, kVSlots = G::kVSlots;
@@ -538,10 +544,25 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const uint16_t* __r
   // Head-major order: consecutive work-groups (spread over all XCDs) share a
   // head; within a head, column block cb of every query tile, then the next.
   const int L = blockIdx.x;
-  const int hc = L / nqt;
-  const int qt = L - hc * nqt;
+  int hc, qt, sp = 0;
+  if constexpr (SPLIT) {  // query tiles fastest, then key ranges, then (head, column block)
+    qt = L % nqt;
+    const int rest = L / nqt;
+    sp = rest % nsplit;
+    hc = rest / nsplit;
+  } else {
+    hc = L / nqt;
+    qt = L - hc * nqt;
+  }
   const int h = hc / kNCB;
   const int cb = hc - h * kNCB;
+  // This work-group's keys [k0, k0 + skv): all of them, or key range sp.
+  int k0 = 0, skv = skv_all;
+  if constexpr (SPLIT) {
+    const int tiles = (skv_all + kBN - 1) / kBN;
+    k0 = int(int64_t(tiles) * sp / nsplit) * kBN;
+    skv = min(skv_all, int(int64_t(tiles) * (sp + 1) / nsplit) * kBN) - k0;
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -553,8 +574,8 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const uint16_t* __r
   const uint16_t* kh = nullptr;
   const uint16_t* vh = nullptr;
   if constexpr (!GV) {
-    kh = kv.k + int64_t(h) * D;
-    vh = kv.v + int64_t(h) * D + cb * DV;
+    kh = kv.k + int64_t(k0) * rowstride + int64_t(h) * D;
+    vh = kv.v + int64_t(k0) * rowstride + int64_t(h) * D + cb * DV;
   }
   const int nT = (skv + kBN - 1) / kBN;
   const bool ragged = (skv % kBN) != 0;
@@ -751,7 +772,18 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const uint16_t* __r
     const float lt = halves_sum(st.l_run[qb]);
     const float inv = 1.f / lt;
     const int row = qrow0 + qb * 32 + col;
-    if (row < sq) {
+    if (SPLIT && row < sq) {
+      float* dst = opart + (int64_t(sp) * sq + row) * rowstride + int64_t(h) * D + cb * DV;
+#pragma unroll
+      for (int db = 0; db < G::kND; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = db * 32 + 8 * g + 4 * hf;
+          *reinterpret_cast<f32x4*>(dst + d0) = f32x4{acc[db][qb][4 * g] * inv, acc[db][qb][4 * g + 1] * inv,
+                                                      acc[db][qb][4 * g + 2] * inv, acc[db][qb][4 * g + 3] * inv};
+        }
+      if (hf == 0 && cb == 0) lse[(int64_t(sp) * H + h) * sq + row] = (st.m_run[qb] + __log2f(lt)) * kLn2;
+    } else if (row < sq) {
       uint16_t* dst = o + int64_t(row) * rowstride + int64_t(h) * D + cb * DV;
 #pragma unroll
       for (int db = 0; db < G::kND; ++db)
@@ -768,15 +800,61 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const uint16_t* __r
   }
 }
 
-template <int D, int DV, bool GV>
+template <int D, int DV, bool GV, bool SPLIT = false>
 hipError_t launch_d(const void* q, const KvArg<GV>& kv, void* o, float* lse, int64_t sq, int64_t skv, int H,
-                    float c, hipStream_t stream) {
+                    float c, hipStream_t stream, int nsplit = 1, float* opart = nullptr) {
   const int64_t nqt = (sq + Geo<D, DV>::BM - 1) / Geo<D, DV>::BM;
-  const int64_t grid = nqt * H * (D / DV);
+  const int64_t grid = nqt * H * (D / DV) * nsplit;
   if (grid > kMaxGrid) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((attn_bf16_kernel<D, DV, GV>), dim3(unsigned(grid)), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((attn_bf16_kernel<D, DV, GV, SPLIT>), dim3(unsigned(grid)), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(q), kv, static_cast<uint16_t*>(o), lse, int(sq), int(skv), H, c,
-                     int(nqt));
+                     int(nqt), nsplit, opart);
+  return hipGetLastError();
+}
+
+// Combines the nsplit partial results of a split launch: with m = max_s lse_s
+// and w_s = exp(lse_s - m), O = sum_s w_s O_s / sum_s w_s (rounded once to
+// bf16) and LSE = m + log(sum_s w_s), all in float32.  One thread per 4
+// output columns of one (row, head).  HBM-bound: reads the partials once.
+__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ opart, const float* __restrict__ lpart,
+                                                    uint16_t* __restrict__ o, float* __restrict__ lse, int nsplit,
+                                                    int64_t sq, int H, int D) {
+  const int64_t g = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int per = D / 4;
+  const int64_t rh = g / per;
+  if (rh >= sq * H) return;
+  const int c4 = int(g - rh * per);
+  const int64_t row = rh / H;
+  const int h = int(rh - row * H);
+  float m = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) m = fmaxf(m, lpart[(int64_t(s) * H + h) * sq + row]);
+  float ws = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < nsplit; ++s) {
+    const float w = expf(lpart[(int64_t(s) * H + h) * sq + row] - m);
+    const f32x4 x = *reinterpret_cast<const f32x4*>(opart + (int64_t(s) * sq * H + rh) * D + 4 * c4);
+    ws += w;
+    acc += w * x;
+  }
+  const float inv = 1.f / ws;
+  u32x2 w2;
+  w2[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  w2[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+  *reinterpret_cast<u32x2*>(o + rh * D + 4 * c4) = w2;
+  if (lse && c4 == 0) lse[int64_t(h) * sq + row] = m + logf(ws);
+}
+
+template <int D, int DV>
+hipError_t launch_split(const void* q, const void* k, const void* v, void* o, float* lse, int64_t sq, int64_t skv,
+                        int H, float c, int nsplit, float* opart, float* lpart, hipStream_t stream) {
+  const KvFlat kv{static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v)};
+  hipError_t e = launch_d<D, DV, false, true>(q, kv, o, lpart, sq, skv, H, c, stream, nsplit, opart);
+  if (e != hipSuccess) return e;
+  const int64_t threads = sq * H * (D / 4);
+  const int64_t blocks = (threads + 255) / 256;
+  if (blocks > kMaxGrid) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(merge_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, opart, lpart,
+                     static_cast<uint16_t*>(o), lse, nsplit, sq, H, D);
   return hipGetLastError();
 }
 
@@ -799,6 +877,16 @@ hipError_t launch_attn_bf16_gv(const void* q, const KvShards& kv, void* o, float
   const int64_t skv = kv.start[kv.W];
   if (d == 64) return launch_d<64, 64, true>(q, kv, o, lse, sq, skv, H, c, stream);
   return launch_d<128, 128, true>(q, kv, o, lse, sq, skv, H, c, stream);
+}
+
+hipError_t launch_attn_bf16_split(const void* q, const void* k, const void* v, void* o, float* lse, int64_t sq,
+                                  int64_t skv, int H, int d, float scale, int nsplit, float* opart, float* lpart,
+                                  hipStream_t stream) {
+  if (sq > (int64_t(1) << 31) - 1024) return hipErrorInvalidValue;
+  const float c = scale * 1.4426950408889634f;
+  if (d == 64) return launch_split<64, 64>(q, k, v, o, lse, sq, skv, H, c, nsplit, opart, lpart, stream);
+  if (d == 512) return launch_split<512, 256>(q, k, v, o, lse, sq, skv, H, c, nsplit, opart, lpart, stream);
+  return launch_split<128, 128>(q, k, v, o, lse, sq, skv, H, c, nsplit, opart, lpart, stream);
 }
 
 }  // namespace spattn

@@ -433,6 +433,52 @@ int shard_attn_fwd(int32_t dtype, const void* q, const void* k, const void* v, v
   return ok();
 }
 
+int64_t sp_attn_split_workspace(int64_t sq, int32_t H, int32_t d, int32_t nsplit) {
+  if (sq < 0 || H < 1 || d < 1 || nsplit < 1) return fail(SP_EINVAL, "sp_attn_split_workspace: bad arguments");
+  int64_t on, ob, ln, lbytes;
+  if (!mul_ok(sq, int64_t(H) * d, &on) || !mul_ok(on, int64_t(nsplit) * 4, &ob) || !mul_ok(sq, int64_t(H), &ln) ||
+      !mul_ok(ln, int64_t(nsplit) * 4, &lbytes) || ob > (int64_t(1) << 60) || lbytes > (int64_t(1) << 60))
+    return fail(SP_ERANGE, "sp_attn_split_workspace: size overflows int64");
+  ok();
+  return ((ob + 255) / 256) * 256 + lbytes;
+}
+
+int shard_attn_fwd_split(int32_t dtype, const void* q, const void* k, const void* v, void* o, float* lse,
+                         int64_t sq, int64_t skv, int32_t H, int32_t d, float scale, int32_t nsplit,
+                         void* workspace, int64_t workspace_bytes, void* stream) {
+  const char* fn = "shard_attn_fwd_split";
+  int64_t qb, kb, lb;
+  if (int rc = check_attn(fn, dtype, sq, skv, H, d, scale, true, &qb, &kb, &lb)) return rc;
+  if (dtype != SP_BF16) return fail(SP_EUNSUPPORTED, "%s: bf16 only", fn);
+  if (nsplit < 1 || nsplit > 1024 || nsplit > (skv + 63) / 64)
+    return fail(SP_EINVAL, "%s: nsplit must be in [1, min(1024, ceil(skv / 64))] (got %d)", fn, nsplit);
+  const int64_t need = sp_attn_split_workspace(sq, H, d, nsplit);
+  if (need < 0) return static_cast<int>(need);
+  if (sq == 0) return ok();
+  if (!q || !k || !v || !o || !workspace) return fail(SP_EINVAL, "%s: null device pointer", fn);
+  if (workspace_bytes < need)
+    return fail(SP_ERANGE, "%s: workspace holds %lld bytes, %lld needed", fn, (long long)workspace_bytes,
+                (long long)need);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(SP_EINVAL, "%s: workspace must be 256-byte aligned", fn);
+  if (ranges_overlap(o, qb, q, qb) || ranges_overlap(o, qb, k, kb) || ranges_overlap(o, qb, v, kb))
+    return fail(SP_EOVERLAP, "%s: o overlaps an input", fn);
+  if (lse && (ranges_overlap(lse, lb, q, qb) || ranges_overlap(lse, lb, k, kb) ||
+              ranges_overlap(lse, lb, v, kb) || ranges_overlap(lse, lb, o, qb)))
+    return fail(SP_EOVERLAP, "%s: lse overlaps another buffer", fn);
+  if (ranges_overlap(workspace, need, q, qb) || ranges_overlap(workspace, need, k, kb) ||
+      ranges_overlap(workspace, need, v, kb) || ranges_overlap(workspace, need, o, qb) ||
+      (lse && ranges_overlap(workspace, need, lse, lb)))
+    return fail(SP_EOVERLAP, "%s: workspace overlaps another buffer", fn);
+  const int64_t ob = sq * H * d * int64_t(nsplit) * 4;
+  float* opart = static_cast<float*>(workspace);
+  float* lpart = reinterpret_cast<float*>(static_cast<char*>(workspace) + ((ob + 255) / 256) * 256);
+  (void)hipGetLastError();
+  hipError_t e = spattn::launch_attn_bf16_split(q, k, v, o, lse, sq, skv, H, d, scale, nsplit, opart, lpart,
+                                                as_stream(stream));
+  if (e != hipSuccess) return hip_fail(e, "split attention launch");
+  return ok();
+}
+
 int shard_attn_fwd_gv(int32_t dtype, const void* q, int32_t W, const void* const* k_shards,
                       const void* const* v_shards, const int64_t* seq_lens, void* o, float* lse, int64_t sq,
                       int32_t H, int32_t d, float scale, void* stream) {

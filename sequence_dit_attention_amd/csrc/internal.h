@@ -54,6 +54,12 @@ struct KvShards {
 
 // Attention against sharded K/V (same results as the gathered call on the
 // concatenation of the shards).
+// Split-key attention: nsplit launches' worth of key ranges in one launch
+// writing float32 partials (opart [nsplit, sq, H, d], lpart [nsplit, H, sq]),
+// then a merge into o (bf16) and lse (may be null).
+hipError_t launch_attn_bf16_split(const void* q, const void* k, const void* v, void* o, float* lse, int64_t sq,
+                                  int64_t skv, int H, int d, float scale, int nsplit, float* opart, float* lpart,
+                                  hipStream_t stream);
 hipError_t launch_attn_bf16_gv(const void* q, const KvShards& kv, void* o, float* lse, int64_t sq, int H, int d,
                                float scale, hipStream_t stream);
 hipError_t launch_attn_f32_gv(const float* q, const KvShards& kv, float* o, float* lse, int64_t sq, int H, int d,

@@ -28,7 +28,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert "shard_attn_fwd" in names and "shard_attn_fwd_gv" in names and len(names) == 15
+    assert "shard_attn_fwd" in names and "shard_attn_fwd_gv" in names and len(names) == 17
     h = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
         assert hasattr(h, n), n
@@ -166,6 +166,26 @@ def test_tile_bounds_match_oracle_and_validation():
     assert g(1, FAKE * 2, 128, 4, 4, 8, 2, 2, None, None) == SP_EINVAL      # null raster
     assert g(1, FAKE * 2, 100, 4, 4, 8, 2, 2, FAKE, None) == SP_ERANGE
     assert g(1, FAKE * 2, 0, 0, 4, 8, 2, 2, None, None) == 0                # nothing to do
+
+
+def test_split_attention_validation():
+    L = _lib.lib()
+    ws = L.sp_attn_split_workspace
+    assert ws(100, 2, 128, 3) == ((3 * 100 * 2 * 128 * 4 + 255) // 256) * 256 + 3 * 2 * 100 * 4
+    assert ws(-1, 2, 128, 3) == SP_EINVAL and ws(10, 2, 128, 0) == SP_EINVAL
+    assert ws(2**40, 2**20, 512, 1024) == SP_ERANGE
+    f = L.shard_attn_fwd_split
+    need = ws(64, 1, 512, 2)
+    W = FAKE * 8  # a workspace address away from the others (256-byte aligned)
+    args = (1, FAKE, FAKE * 2, FAKE * 3, FAKE * 4, None, 64, 300, 1, 512, 0.04)
+    assert f(*args, 0, W, need, None) == SP_EINVAL                  # nsplit < 1
+    assert f(*args, 6, W, 10**9, None) == SP_EINVAL                 # more ranges than 64-key tiles
+    assert f(*args, 2, W, need - 1, None) == SP_ERANGE              # workspace too small
+    assert f(*args, 2, W + 16, need, None) == SP_EINVAL             # misaligned
+    assert f(*args, 2, None, need, None) == SP_EINVAL               # null workspace
+    assert f(*args, 2, FAKE * 4, need, None) == SP_EOVERLAP         # workspace on top of o
+    assert f(0, FAKE, FAKE * 2, FAKE * 3, FAKE * 4, None, 64, 300, 1, 128, 0.08, 2, W, need, None) == SP_EUNSUPPORTED
+    assert f(1, FAKE, FAKE * 2, FAKE * 3, FAKE * 4, None, 64, 300, 1, 256, 0.06, 2, W, need, None) == SP_EUNSUPPORTED
 
 
 def test_av_positions_match_oracle():
