@@ -89,6 +89,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="p768_15s_w4")
     ap.add_argument("--cpu-rows", type=int, default=192, help="query rows in the CPU-oracle sample (0: skip)")
+    ap.add_argument("--vae-steps", type=int, default=3, help="timed steps of the VAE block-split share (0: skip)")
     ap.add_argument("--gf-steps", type=int, default=2,
                     help="steps of the gather-free variant timed after the headline steps (0: skip)")
     args = ap.parse_args()
@@ -103,7 +104,7 @@ def main() -> int:
 
     from sequence_dit_attention_amd import api
     from sequence_dit_attention_amd.pipeline import RankShare
-    from synth import gen_gamma, gen_qkv, get_workload
+    from synth import gen_gamma, gen_qkv, gen_tensor, get_workload
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -226,6 +227,37 @@ def main() -> int:
     qn_gbs = 2 * xn.numel() * xn.element_size() / (ms * 1e-3) / 1e9
     qnr = {"q_ms": ms, "gbs": qn_gbs, "frac_hbm_peak": qn_gbs / PEAK_HBM_GBS, "eps": 1e-6}
 
+    # The VAE's attention under the spatial block split: process 0 of a 128 x 128
+    # latent feature map with 512 channels cut into 2 x 2 blocks (reported
+    # beside the headline step; a second workload, not part of it).
+    vae = None
+    if args.vae_steps > 0:
+        from sequence_dit_attention_amd.pipeline import VaeBlockShare
+        vs = VaeBlockShare(128, 128, 512, 2, 2, 0, nsplit=4)
+        gq, gk, gv = (gen_tensor(wl.seed + 100, t, vs.n, 1, vs.C, "bf16") for t in range(3))
+        dev_bf16 = lambda a: torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16).view(128, 128, 512)
+        vs.set_inputs(dev_bf16(gq), dev_bf16(gk), dev_bf16(gv))
+        vs.step()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.vae_steps)]
+        for i in range(args.vae_steps):
+            ev[i][0].record()
+            vs.gather_kv()
+            ev[i][1].record()
+            vs.attend()
+            ev[i][2].record()
+            vs.place_out()
+            ev[i][3].record()
+        torch.cuda.synchronize()
+        vms = [sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.vae_steps)) / args.vae_steps
+               for j in range(3)]
+        va_tf = vs.attn_flops() / (vms[1] * 1e-3) / 1e12
+        vae = {"workload": "vae_128x128_c512_blocks2x2_p0", "sq": vs.m, "skv": vs.n, "d": vs.C, "nsplit": vs.nsplit,
+               "ms_per_step": sum(vms), "gather_kv_ms": vms[0], "attn_ms": vms[1], "place_out_ms": vms[2],
+               "attn_tflops": va_tf, "attn_frac_mfma_peak": va_tf / PEAK_BF16_TFLOPS,
+               "copy_gbs": vs.copy_bytes() / ((vms[0] + vms[2]) * 1e-3) / 1e9}
+        log(f"VAE block share: {sum(vms):.3f} ms (attention {vms[1]:.3f} ms, {va_tf:.0f} TFLOP/s)")
+
     flops = share.attn_flops()
     attn_tflops = flops / (per["attn"] * 1e-3) / 1e12
     pack_bytes = share.pack_kv_bytes()
@@ -259,6 +291,7 @@ def main() -> int:
         "gather_free": gf,
         "rope_multi_axis": rmx,
         "qk_norm_rope": qnr,
+        "vae_block_attention": vae,
     }
     if args.cpu_rows > 0:
         log(f"CPU oracle baseline on {args.cpu_rows} rows")

@@ -108,3 +108,76 @@ class RankShare:
     def pack_kv_bytes(self) -> int:
         """Read + write bytes of the K and V pack (one AllGatherV of each)."""
         return 2 * 2 * self.S * self.inner * self.flat_k.element_size()
+
+
+class VaeBlockShare:
+    """Process p's share of the VAE's attention under the spatial block split.
+
+    Page NPU HunyuanImage-3.0模型推理优化实践, section VAE并行优化: the feature
+    map is cut along height and width into pr x pc blocks, one per process;
+    attention gathers the K and V of all blocks; the outputs are gathered back
+    in two stages and put at their spatial positions.  Per step:
+      1. gather of the K and V blocks in process order (tile_pack of the
+         channels-last rasters: the AllGatherV receive buffers),
+      2. attention of process p's block queries against all gathered keys,
+         one head over the C channels, keys cut into nsplit ranges,
+         written straight into p's slot of the flat output,
+      3. second stage of the output gather: the flat blocks back into the
+         raster (tile_unpack); the other processes' output blocks are
+         stand-ins, as on a real run they come from their own GPUs.
+    Process p's query block is prepared at set-up (on a real run the 1x1
+    projections produce it locally).
+    """
+
+    def __init__(self, Hh: int, Ww: int, C: int, pr: int, pc: int, p: int, nsplit: int,
+                 dtype: torch.dtype = torch.bfloat16, device="cuda"):
+        self.Hh, self.Ww, self.C, self.pr, self.pc, self.p, self.nsplit = Hh, Ww, C, pr, pc, p, nsplit
+        self.n = Hh * Ww
+        self.blocks = [api.sp_tile_bounds(Hh, Ww, pr, pc, i) for i in range(pr * pc)]
+        sizes = [(r1 - r0) * (c1 - c0) for r0, r1, c0, c1 in self.blocks]
+        self.off = sum(sizes[:p])
+        self.m = sizes[p]
+        e = dict(dtype=dtype, device=torch.device(device))
+        self.k_flat = torch.empty(self.n, C, **e)
+        self.v_flat = torch.empty(self.n, C, **e)
+        self.o_flat = torch.zeros(self.n, C, **e)
+        self.o = torch.empty(Hh, Ww, C, **e)
+        self.q_block = torch.empty(self.m, C, **e)
+        self.workspace = torch.empty(api.split_workspace_bytes(self.m, 1, C, nsplit), dtype=torch.uint8,
+                                     device=torch.device(device))
+        self.q = self.k = self.v = None
+
+    def set_inputs(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor) -> None:
+        """Channels-last rasters [Hh, Ww, C]; process p's query block is cut out once here."""
+        for t in (q, k, v):
+            if t.shape != (self.Hh, self.Ww, self.C) or not t.is_contiguous():
+                raise ValueError("inputs must be contiguous [Hh, Ww, C]")
+        self.q, self.k, self.v = q, k, v
+        flat = api.tile_pack(q, self.pr, self.pc)
+        self.q_block.copy_(flat[self.off:self.off + self.m])
+
+    def gather_kv(self) -> None:
+        api.tile_pack(self.k, self.pr, self.pc, self.k_flat)
+        api.tile_pack(self.v, self.pr, self.pc, self.v_flat)
+
+    def attend(self) -> None:
+        C = self.C
+        api.shard_attn_fwd_split(self.q_block.view(self.m, 1, C), self.k_flat.view(self.n, 1, C),
+                                 self.v_flat.view(self.n, 1, C), self.nsplit,
+                                 out=self.o_flat[self.off:self.off + self.m].view(self.m, 1, C),
+                                 workspace=self.workspace)
+
+    def place_out(self) -> None:
+        api.tile_unpack(self.o_flat, self.Hh, self.Ww, self.pr, self.pc, self.o)
+
+    def step(self) -> None:
+        self.gather_kv()
+        self.attend()
+        self.place_out()
+
+    def attn_flops(self) -> int:
+        return 4 * self.m * self.n * self.C
+
+    def copy_bytes(self) -> int:
+        """Read + write bytes of the K and V gathers and of the output placement."""
+        return 3 * 2 * self.n * self.C * self.k_flat.element_size()

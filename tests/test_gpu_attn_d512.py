@@ -97,3 +97,25 @@ def test_vae_block_split_attention(Hh, Ww, pr, pc):
     ro, _ = oracle.attention(to_f64(q).reshape(n, 1, C), to_f64(k).reshape(n, 1, C), to_f64(v).reshape(n, 1, C))
     _bf16_ok(to_f64(o).reshape(n, 1, C), ro)
     _bf16_ok(to_f64(whole), ro)
+
+
+def test_vae_block_share_step():
+    """The pipeline's step for process 4 of a 40 x 36 map cut 2 x 3: gather, split attention into the
+    process's slot, placement; its block of the output raster matches the oracle, other blocks keep
+    their stand-in zeros."""
+    from sequence_dit_attention_amd.pipeline import VaeBlockShare
+    Hh, Ww, C, pr, pc, p = 40, 36, 512, 2, 3, 4
+    n = Hh * Ww
+    q, k, v = (gen_tensor(24, t, n, 1, C, "bf16").reshape(Hh, Ww, C) for t in range(3))
+    vs = VaeBlockShare(Hh, Ww, C, pr, pc, p, nsplit=3)
+    vs.set_inputs(*(to_dev(t, "bf16") for t in (q, k, v)))
+    vs.step()
+    torch.cuda.synchronize()
+    got = to_f64(vs.o)
+    r0, r1, c0, c1 = oracle.tile_bounds(Hh, Ww, pr, pc, p)
+    qb = to_f64(q)[r0:r1, c0:c1].reshape(-1, 1, C)
+    ro, _ = oracle.attention(qb, to_f64(k).reshape(n, 1, C), to_f64(v).reshape(n, 1, C))
+    _bf16_ok(got[r0:r1, c0:c1].reshape(-1, 1, C), ro)
+    mask = np.ones((Hh, Ww), dtype=bool)
+    mask[r0:r1, c0:c1] = False
+    assert np.all(got[mask] == 0.0)
