@@ -219,9 +219,12 @@ int tile_unpack(int32_t dtype, const void* flat, int64_t flat_elems, int64_t Hh,
  *   pos       NULL, or device int64 [s, 3] as in rope_apply_mx
  *   sections  host array of 3 pair counts (only read when pos is not NULL)
  * Errors: as rope_apply / rope_apply_mx, plus SP_EINVAL (eps negative or not
- * finite, null gamma with data), SP_EUNSUPPORTED (d/2 not splittable into at
- * most 64 lanes of 1, 2, 4 or 8 pairs: every even d up to 128, every d up to
- * 1024 with d/2 a multiple of 8), SP_EOVERLAP (gamma or pos overlaps y).
+ * finite, null gamma with data), SP_EUNSUPPORTED (a head row must split into
+ * at most 64 lanes of g = 1, 2, 4 or 8 pairs with x and y aligned to g
+ * elements, 2g for SP_ROPE_INTERLEAVED with g > 1: every even d up to 128
+ * qualifies for any buffers, and every d up to 1024 with d/2 a multiple of 8
+ * for 32-byte aligned ones, such as torch's allocations), SP_EOVERLAP (gamma
+ * or pos overlaps y).
  */
 int qk_norm_rope(int32_t dtype, const void* x, void* y, int64_t s, int32_t H, int32_t d, const float* gamma,
                  double eps, int64_t pos0, const int64_t* pos, const int32_t* sections, double theta, int32_t style,

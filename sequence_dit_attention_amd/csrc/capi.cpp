@@ -355,8 +355,6 @@ int qk_norm_rope(int32_t dtype, const void* x, void* y, int64_t s, int32_t H, in
   if (style != SP_ROPE_HALF && style != SP_ROPE_INTERLEAVED) return fail(SP_EINVAL, "%s: unknown style %d", fn, style);
   if (s < 0 || H < 1) return fail(SP_EINVAL, "%s: need s >= 0 and H >= 1", fn);
   if (d < 2 || d > 1024 || (d & 1)) return fail(SP_EINVAL, "%s: d must be even, 2..1024 (got %d)", fn, d);
-  if (!spattn::norm_pairs_per_lane(d))
-    return fail(SP_EUNSUPPORTED, "%s: d = %d does not split into at most 64 lanes of 1, 2, 4 or 8 pairs", fn, d);
   if (!(std::isfinite(theta) && theta > 0.0)) return fail(SP_EINVAL, "%s: theta must be finite and > 0", fn);
   if (!(std::isfinite(eps) && eps >= 0.0 && eps <= 3.0e38)) return fail(SP_EINVAL, "%s: eps must be finite and >= 0", fn);
   if (pos) {
@@ -376,6 +374,10 @@ int qk_norm_rope(int32_t dtype, const void* x, void* y, int64_t s, int32_t H, in
   if (x != y && ranges_overlap(x, bytes, y, bytes)) return fail(SP_EOVERLAP, "%s: x and y overlap without being equal", fn);
   if (ranges_overlap(gamma, int64_t(d) * 4, y, bytes)) return fail(SP_EOVERLAP, "%s: gamma overlaps y", fn);
   if (pos && ranges_overlap(pos, pbytes, y, bytes)) return fail(SP_EOVERLAP, "%s: positions overlap y", fn);
+  if (!spattn::rows_pairs_per_lane(d, style, eb, x, y))
+    return fail(SP_EUNSUPPORTED,
+                "%s: d = %d with these buffers: a head row must split into at most 64 lanes of 1, 2, 4 or 8 pairs "
+                "with x and y aligned to that many elements", fn, d);
   const int sec[3] = {pos ? sections[0] : d / 2, pos ? sections[1] : 0, pos ? sections[2] : 0};
   (void)hipGetLastError();
   hipError_t e = spattn::launch_qk_norm_rope(dtype, x, y, s, H, d, gamma, static_cast<float>(eps), pos0, pos, sec,

@@ -28,9 +28,11 @@ hipError_t launch_rope(int dtype, const void* x, void* y, int64_t s, int H, int 
 hipError_t launch_rope_mx(int dtype, const void* x, void* y, int64_t s, int H, int d, const int64_t* pos,
                           const int* sections, double theta, int style, hipStream_t stream);
 
-// Pairs per lane of the fused RMSNorm + RoPE kernel for head size d (the head
-// row must fit one wave: d/2 pairs in at most 64 lanes); 0 if unsupported.
-int norm_pairs_per_lane(int d);
+// Pairs per lane of the one-wave-per-token RoPE kernels for head size d,
+// pairing style (0 half, 1 interleaved), element bytes eb and the buffers x, y
+// (their addresses must suit the vector accesses); 0 if the head row does not
+// fit one wave in groups of 1, 2, 4 or 8 pairs with aligned accesses.
+int rows_pairs_per_lane(int d, int style, int eb, const void* x, const void* y);
 hipError_t launch_qk_norm_rope(int dtype, const void* x, void* y, int64_t s, int H, int d, const float* gamma,
                                float eps, int64_t pos0, const int64_t* pos, const int* sections, double theta,
                                int style, hipStream_t stream);

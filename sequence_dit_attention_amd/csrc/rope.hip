@@ -1,16 +1,18 @@
-// Rotary position embedding of one rank's local slice at absolute positions.
+// Rotary position embedding of one rank's local slice at absolute positions,
+// and the per-head RMSNorm fused in front of it.
 //
 // Page "HCCL AllGatherV 实战解析：MiniMax-H3-Comfy-NPU ...", section 机制一: the
 // RoPE frequency table is sliced with the rank's token range, so token t of
 // the slice rotates at position pos0 + t.  Page "NPU HunyuanImage-3.0模型推理优化
-// 实践", section 消除旋转位置编码冗余cast算子: the rotation applies to q and k.
+// 实践", section 消除旋转位置编码冗余cast算子: the rotation applies to q and k;
+// sections 计算分解 and RmsNorm算子优化: q and k heads are normalised over the
+// head dimension, scaled by a learned weight, then rotated.
 //
-// Each thread owns PG consecutive frequency pairs of one token: it derives the
-// angles p * theta^(-2j/d) and their cos/sin once in float64 (positions reach
-// 3.7e5 here, where a float32 angle would be off by up to 0.03 rad) and then
-// walks all H heads of that token, so the float64 work is shared by H rows.
-// The rotation itself is float32; the result is rounded to the storage type
-// (nearest-even).  HBM-bound: each element is read once and written once.
+// Angles p * theta^(-2j/d) and their range reduction are float64 (positions
+// reach 3.7e5 here, where a float32 angle would be off by up to 0.03 rad);
+// cos/sin are rounded to float32, the norm and the rotation are float32 and
+// the result is rounded once to the storage type (nearest-even).  HBM-bound:
+// each element is read once and written once.
 #include <hip/hip_bf16.h>
 
 #include "internal.h"
@@ -29,6 +31,45 @@ __device__ inline uint16_t to_bf16(float f) {
 }
 __device__ inline void st(float* p, float f) { *p = f; }
 __device__ inline void st(uint16_t* p, float f) { *p = to_bf16(f); }
+__device__ inline float widen(float v) { return v; }
+__device__ inline float widen(uint16_t v) { return __uint_as_float(uint32_t(v) << 16); }
+__device__ inline float narrow(float f, float*) { return f; }
+__device__ inline uint16_t narrow(float f, uint16_t*) { return to_bf16(f); }
+
+// N consecutive elements as one vector access, non-temporal (every element is
+// touched once).  Written out explicitly: element-wise bf16 accesses are not
+// merged by the compiler and run at two thirds of the vector rate.
+template <typename T, int N>
+struct Vec {
+  typedef T type __attribute__((ext_vector_type(N)));
+};
+template <typename T>
+struct Vec<T, 1> {
+  typedef T type;
+};
+template <int N, typename T>
+__device__ inline void ldv(const T* p, float (&o)[N]) {
+  typedef typename Vec<T, N>::type V;
+  const V v = __builtin_nontemporal_load(reinterpret_cast<const V*>(p));
+  if constexpr (N == 1) {
+    o[0] = widen(v);
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) o[i] = widen(T(v[i]));
+  }
+}
+template <int N, typename T>
+__device__ inline void stv(T* p, const float (&f)[N]) {
+  typedef typename Vec<T, N>::type V;
+  V v;
+  if constexpr (N == 1) {
+    v = narrow(f[0], p);
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = narrow(f[i], p);
+  }
+  __builtin_nontemporal_store(v, reinterpret_cast<V*>(p));
+}
 
 // cos/sin of the PG pairs j0 .. j0+PG-1 of token t.
 // Multi-axis form: the d/2 pairs are split into consecutive groups of n0, n1
@@ -54,70 +95,18 @@ __device__ inline void pair_angles(int64_t t, int j0, int half, int64_t pos0, co
   }
 }
 
+// The rotation of pair (x1, x2), each output rounded once from an explicit
+// fused multiply-add: the same bits whichever kernel or access width computes
+// it (left to the compiler, the contraction of a*c - b*s varies with the
+// shape of the surrounding code).
+__device__ inline float rot_first(float x1, float x2, float c, float s) { return fmaf(x1, c, -(x2 * s)); }
+__device__ inline float rot_second(float x1, float x2, float c, float s) { return fmaf(x2, c, x1 * s); }
+
 // Element offsets inside a head row of the two members of pair j.
 template <bool INTERLEAVED>
 __device__ inline int first_of(int j, int half) { return INTERLEAVED ? 2 * j : j; }
 template <bool INTERLEAVED>
 __device__ inline int second_of(int j, int half) { return INTERLEAVED ? 2 * j + 1 : j + half; }
-
-// PG pairs per thread; element loads/stores are PG (or 2*PG) contiguous values
-// and the compiler merges them into vector accesses when aligned.
-template <typename T, int PG, bool INTERLEAVED>
-__global__ __launch_bounds__(kThreads) void rope_kernel(const T* x, T* y, int64_t s, int H, int d, int64_t pos0,
-                                                        const int64_t* __restrict__ pos, int n0, int n1,
-                                                        double log2theta) {
-  const int half = d >> 1;
-  const int groups = half / PG;
-  const int64_t g = int64_t(blockIdx.x) * kThreads + threadIdx.x;
-  const int64_t t = g / groups;
-  if (t >= s) return;
-  const int j0 = int(g - t * groups) * PG;
-
-  float cs[PG], sn[PG];
-  pair_angles<PG>(t, j0, half, pos0, pos, n0, n1, log2theta, cs, sn);
-
-  // Heads are processed in batches of HB: all loads of a batch are issued
-  // before its stores.  x and y are either the same buffer or disjoint, and
-  // every element is read and written by this thread only, so reading ahead
-  // of the stores is safe in place too (the compiler cannot prove it, so the
-  // batching is explicit).
-  constexpr int HB = 8;
-  for (int h0 = 0; h0 < H; h0 += HB) {
-    float a[HB][PG], b[HB][PG];
-#pragma unroll
-    for (int hh = 0; hh < HB; ++hh) {
-      if (h0 + hh >= H) break;
-      const int64_t row = (t * H + h0 + hh) * int64_t(d);
-#pragma unroll
-      for (int u = 0; u < PG; ++u) {
-        if (INTERLEAVED) {
-          a[hh][u] = ld(x + row + 2 * (j0 + u));
-          b[hh][u] = ld(x + row + 2 * (j0 + u) + 1);
-        } else {
-          a[hh][u] = ld(x + row + j0 + u);
-          b[hh][u] = ld(x + row + half + j0 + u);
-        }
-      }
-    }
-#pragma unroll
-    for (int hh = 0; hh < HB; ++hh) {
-      if (h0 + hh >= H) break;
-      const int64_t row = (t * H + h0 + hh) * int64_t(d);
-#pragma unroll
-      for (int u = 0; u < PG; ++u) {
-        const float ya = a[hh][u] * cs[u] - b[hh][u] * sn[u];
-        const float yb = b[hh][u] * cs[u] + a[hh][u] * sn[u];
-        if (INTERLEAVED) {
-          st(y + row + 2 * (j0 + u), ya);
-          st(y + row + 2 * (j0 + u) + 1, yb);
-        } else {
-          st(y + row + j0 + u, ya);
-          st(y + row + half + j0 + u, yb);
-        }
-      }
-    }
-  }
-}
 
 // v + (v of the partner lane selected by the DPP control CTRL).
 template <int CTRL>
@@ -156,153 +145,256 @@ __device__ inline void group_sums(float (&v)[N], int L) {
   }
 }
 
-// Per-head RMSNorm followed by the rotation (page "NPU HunyuanImage-3.0模型推理
-// 优化实践", sections 计算分解 and RmsNorm算子优化: q and k heads are
-// normalised over the head dimension, scaled by a learned weight, then
-// rotated).  Token t's head row is spread over L = 2^lanes_log2 consecutive
-// lanes of one wave (L >= d/2/PG, lanes beyond d/2/PG hold zeros and store
-// nothing); each lane squares and sums its 2*PG elements, group_sums adds
-// them across the L lanes so that every lane holds the same row sum, then
-//   y = rotate(x * gamma / sqrt(sum(x^2) / d + eps))
-// in float32, rounded once to the storage type.  One read and one write per
-// element, like rope_kernel.
-template <typename T, int PG, bool INTERLEAVED>
-__global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(const T* x, T* y, int64_t s, int H, int d,
-                                                                int lanes_log2, const float* __restrict__ gamma,
-                                                                float eps, int64_t pos0,
-                                                                const int64_t* __restrict__ pos, int n0, int n1,
-                                                                double log2theta) {
+// One wave per token.  Its 64 lanes form R = 64 / L row slots of L lanes
+// (L = 2^lanes_log2 >= d/2/PG); slot r handles heads r, r + R, r + 2R, ... of
+// the token, so each load instruction of the wave covers R consecutive head
+// rows, and lane jg of a slot owns pairs jg*PG .. jg*PG+PG-1 (lanes past
+// d/2/PG read pair 0 and store nothing).  A lane's PG first and PG second
+// pair members are contiguous (2*PG for the interleaved pairing), so they move
+// as vectors.  With d/2 <= 64 each lane derives the cos/sin of one pair and
+// the wave shares them by lane shuffles: every angle of a token is computed
+// once.  NORM: each lane squares and sums its 2*PG elements, group_sums adds
+// them across the row's L lanes, and y = rotate(x * gamma / sqrt(sum / d + eps)).
+// Heads are processed in batches of HB iterations with all loads of a batch
+// before its stores: in place is allowed, and each element is read and
+// written by one lane only.
+template <typename T, int PG, bool IL, bool NORM>
+__global__ __launch_bounds__(kThreads) void rope_rows_kernel(const T* x, T* y, int64_t s, int H, int d,
+                                                             int lanes_log2, const float* __restrict__ gamma,
+                                                             float eps, int64_t pos0,
+                                                             const int64_t* __restrict__ pos, int n0, int n1,
+                                                             double log2theta) {
   const int half = d >> 1;
   const int groups = half / PG;
-  const int L = 1 << lanes_log2;
-  const int64_t g = int64_t(blockIdx.x) * kThreads + threadIdx.x;
-  const int64_t t = g >> lanes_log2;
-  if (t >= s) return;  // whole L-lane groups leave together, so the butterflies below stay inside live groups
-  const int jg = int(g & (L - 1));
+  const int L = 1 << lanes_log2, R = 64 >> lanes_log2;
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t(blockIdx.x) * kThreads + threadIdx.x) >> 6;
+  if (t >= s) return;  // whole waves leave together
+  const int slot = lane >> lanes_log2, jg = lane & (L - 1);
   const bool act = jg < groups;
   const int j0 = (act ? jg : 0) * PG;
 
-  float cs[PG], sn[PG], ga[PG], gb[PG];
-  pair_angles<PG>(t, j0, half, pos0, pos, n0, n1, log2theta, cs, sn);
+  float cs[PG], sn[PG];
+  if (half <= 64) {
+    float c1[1], s1[1];
+    pair_angles<1>(t, lane < half ? lane : 0, half, pos0, pos, n0, n1, log2theta, c1, s1);
 #pragma unroll
-  for (int u = 0; u < PG; ++u) {
-    ga[u] = gamma[first_of<INTERLEAVED>(j0 + u, half)];
-    gb[u] = gamma[second_of<INTERLEAVED>(j0 + u, half)];
+    for (int u = 0; u < PG; ++u) {
+      cs[u] = __shfl(c1[0], j0 + u);
+      sn[u] = __shfl(s1[0], j0 + u);
+    }
+  } else {
+    pair_angles<PG>(t, j0, half, pos0, pos, n0, n1, log2theta, cs, sn);
+  }
+  float ga[PG], gb[PG];
+  if constexpr (NORM) {
+#pragma unroll
+    for (int u = 0; u < PG; ++u) {
+      ga[u] = gamma[first_of<IL>(j0 + u, half)];
+      gb[u] = gamma[second_of<IL>(j0 + u, half)];
+    }
   }
   const float fd = float(d);
-
-  // Heads in batches of HB with all loads of a batch before its stores; safe
-  // in place for the same reason as in rope_kernel.
-  constexpr int HB = 8;
-  for (int h0 = 0; h0 < H; h0 += HB) {
+  const int nk = (H + R - 1) / R;  // head iterations of a slot
+  constexpr int HB = 6;            // iterations per batch (24 heads of 128: one batch)
+  for (int k0 = 0; k0 < nk; k0 += HB) {
     float a[HB][PG], b[HB][PG], ss[HB];
 #pragma unroll
-    for (int hh = 0; hh < HB; ++hh) ss[hh] = 0.f;
+    for (int kk = 0; kk < HB; ++kk) ss[kk] = 0.f;
 #pragma unroll
-    for (int hh = 0; hh < HB; ++hh) {
-      // a last batch past head H-1 re-reads head H-1 and stores nothing for
-      // it, and idle lanes read pair 0 and drop it: every load stays
-      // unconditional, so the loads vectorise and need no branch
-      const int64_t row = (t * H + min(h0 + hh, H - 1)) * int64_t(d);
+    for (int kk = 0; kk < HB; ++kk) {
+      if (k0 + kk >= nk) break;
+      // a slot past head H-1 re-reads head H-1 and stores nothing
+      const T* row = x + (t * H + min((k0 + kk) * R + slot, H - 1)) * int64_t(d);
+      if constexpr (IL && PG == 1) {  // one pair: two element accesses, element alignment suffices
+        float va[1], vb[1];
+        ldv<1>(row + 2 * j0, va);
+        ldv<1>(row + 2 * j0 + 1, vb);
+        a[kk][0] = act ? va[0] : 0.f;
+        b[kk][0] = act ? vb[0] : 0.f;
+      } else if constexpr (IL) {
+        float v[2 * PG];
+        ldv<2 * PG>(row + 2 * j0, v);
 #pragma unroll
-      for (int u = 0; u < PG; ++u) {
-        const float va = ld(x + row + first_of<INTERLEAVED>(j0 + u, half));
-        const float vb = ld(x + row + second_of<INTERLEAVED>(j0 + u, half));
-        a[hh][u] = act ? va : 0.f;
-        b[hh][u] = act ? vb : 0.f;
-        ss[hh] += a[hh][u] * a[hh][u] + b[hh][u] * b[hh][u];
+        for (int u = 0; u < PG; ++u) {
+          a[kk][u] = act ? v[2 * u] : 0.f;
+          b[kk][u] = act ? v[2 * u + 1] : 0.f;
+        }
+      } else {
+        float va[PG], vb[PG];
+        ldv<PG>(row + j0, va);
+        ldv<PG>(row + half + j0, vb);
+#pragma unroll
+        for (int u = 0; u < PG; ++u) {
+          a[kk][u] = act ? va[u] : 0.f;
+          b[kk][u] = act ? vb[u] : 0.f;
+        }
+      }
+      if constexpr (NORM) {
+#pragma unroll
+        for (int u = 0; u < PG; ++u) ss[kk] = fmaf(b[kk][u], b[kk][u], fmaf(a[kk][u], a[kk][u], ss[kk]));
       }
     }
-    group_sums(ss, L);
+    if constexpr (NORM) group_sums(ss, L);
 #pragma unroll
-    for (int hh = 0; hh < HB; ++hh) {
-      if (!act || h0 + hh >= H) break;
-      const int64_t row = (t * H + h0 + hh) * int64_t(d);
-      const float r = 1.0f / sqrtf(ss[hh] / fd + eps);
+    for (int kk = 0; kk < HB; ++kk) {
+      if (k0 + kk >= nk) break;
+      const int h = (k0 + kk) * R + slot;
+      if (!act || h >= H) continue;
+      T* row = y + (t * H + h) * int64_t(d);
+      float r = 1.f;
+      if constexpr (NORM) r = 1.0f / sqrtf(ss[kk] / fd + eps);
+      float ya[PG], yb[PG];
 #pragma unroll
       for (int u = 0; u < PG; ++u) {
-        const float na = a[hh][u] * r * ga[u];
-        const float nb = b[hh][u] * r * gb[u];
-        st(y + row + first_of<INTERLEAVED>(j0 + u, half), na * cs[u] - nb * sn[u]);
-        st(y + row + second_of<INTERLEAVED>(j0 + u, half), nb * cs[u] + na * sn[u]);
+        const float na = NORM ? a[kk][u] * r * ga[u] : a[kk][u];
+        const float nb = NORM ? b[kk][u] * r * gb[u] : b[kk][u];
+        ya[u] = rot_first(na, nb, cs[u], sn[u]);
+        yb[u] = rot_second(na, nb, cs[u], sn[u]);
+      }
+      if constexpr (IL && PG == 1) {
+        stv<1>(row + 2 * j0, ya);
+        stv<1>(row + 2 * j0 + 1, yb);
+      } else if constexpr (IL) {
+        float v[2 * PG];
+#pragma unroll
+        for (int u = 0; u < PG; ++u) {
+          v[2 * u] = ya[u];
+          v[2 * u + 1] = yb[u];
+        }
+        stv<2 * PG>(row + 2 * j0, v);
+      } else {
+        stv<PG>(row + j0, ya);
+        stv<PG>(row + half + j0, yb);
       }
     }
   }
 }
 
-template <typename T, int PG, bool IL>
-hipError_t launch_norm_typed(const void* x, void* y, int64_t s, int H, int d, const float* gamma, float eps,
-                             int64_t pos0, const int64_t* pos, int n0, int n1, double l2t, hipStream_t stream) {
+// General shapes (a head row that does not fit one wave in groups of 1, 2, 4
+// or 8 pairs, or buffers not aligned for the vector accesses): each thread
+// owns PG consecutive pairs of one token and walks all H heads of that token,
+// element by element.  Same arithmetic as rope_rows_kernel without NORM.
+template <typename T, int PG, bool INTERLEAVED>
+__global__ __launch_bounds__(kThreads) void rope_kernel(const T* x, T* y, int64_t s, int H, int d, int64_t pos0,
+                                                        const int64_t* __restrict__ pos, int n0, int n1,
+                                                        double log2theta) {
+  const int half = d >> 1;
+  const int groups = half / PG;
+  const int64_t g = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t t = g / groups;
+  if (t >= s) return;
+  const int j0 = int(g - t * groups) * PG;
+
+  float cs[PG], sn[PG];
+  pair_angles<PG>(t, j0, half, pos0, pos, n0, n1, log2theta, cs, sn);
+
+  constexpr int HB = 8;
+  for (int h0 = 0; h0 < H; h0 += HB) {
+    float a[HB][PG], b[HB][PG];
+#pragma unroll
+    for (int hh = 0; hh < HB; ++hh) {
+      if (h0 + hh >= H) break;
+      const int64_t row = (t * H + h0 + hh) * int64_t(d);
+#pragma unroll
+      for (int u = 0; u < PG; ++u) {
+        a[hh][u] = ld(x + row + first_of<INTERLEAVED>(j0 + u, half));
+        b[hh][u] = ld(x + row + second_of<INTERLEAVED>(j0 + u, half));
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < HB; ++hh) {
+      if (h0 + hh >= H) break;
+      const int64_t row = (t * H + h0 + hh) * int64_t(d);
+#pragma unroll
+      for (int u = 0; u < PG; ++u) {
+        st(y + row + first_of<INTERLEAVED>(j0 + u, half), rot_first(a[hh][u], b[hh][u], cs[u], sn[u]));
+        st(y + row + second_of<INTERLEAVED>(j0 + u, half), rot_second(a[hh][u], b[hh][u], cs[u], sn[u]));
+      }
+    }
+  }
+}
+
+template <typename T, int PG, bool IL, bool NORM>
+hipError_t launch_rows(const void* x, void* y, int64_t s, int H, int d, const float* gamma, float eps, int64_t pos0,
+                       const int64_t* pos, int n0, int n1, double l2t, hipStream_t stream) {
   const int groups = (d / 2) / PG;
   int lg = 0;
   while ((1 << lg) < groups) ++lg;
-  const int64_t threads = s << lg;
-  const int64_t blocks = (threads + kThreads - 1) / kThreads;
+  const int64_t blocks = (s + kThreads / 64 - 1) / (kThreads / 64);  // one wave per token
   if (blocks > kMaxGrid) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((qk_norm_rope_kernel<T, PG, IL>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
+  hipLaunchKernelGGL((rope_rows_kernel<T, PG, IL, NORM>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
                      stream, static_cast<const T*>(x), static_cast<T*>(y), s, H, d, lg, gamma, eps, pos0, pos, n0,
                      n1, l2t);
   return hipGetLastError();
 }
 
-template <typename T, bool IL>
-hipError_t launch_norm_pg(const void* x, void* y, int64_t s, int H, int d, const float* gamma, float eps,
+template <typename T, bool IL, bool NORM>
+hipError_t launch_rows_pg(int pg, const void* x, void* y, int64_t s, int H, int d, const float* gamma, float eps,
                           int64_t pos0, const int64_t* pos, int n0, int n1, double l2t, hipStream_t stream) {
-  switch (norm_pairs_per_lane(d)) {
-    case 4: return launch_norm_typed<T, 4, IL>(x, y, s, H, d, gamma, eps, pos0, pos, n0, n1, l2t, stream);
-    case 8: return launch_norm_typed<T, 8, IL>(x, y, s, H, d, gamma, eps, pos0, pos, n0, n1, l2t, stream);
-    case 2: return launch_norm_typed<T, 2, IL>(x, y, s, H, d, gamma, eps, pos0, pos, n0, n1, l2t, stream);
-    case 1: return launch_norm_typed<T, 1, IL>(x, y, s, H, d, gamma, eps, pos0, pos, n0, n1, l2t, stream);
+  switch (pg) {
+    case 4: return launch_rows<T, 4, IL, NORM>(x, y, s, H, d, gamma, eps, pos0, pos, n0, n1, l2t, stream);
+    case 8: return launch_rows<T, 8, IL, NORM>(x, y, s, H, d, gamma, eps, pos0, pos, n0, n1, l2t, stream);
+    case 2: return launch_rows<T, 2, IL, NORM>(x, y, s, H, d, gamma, eps, pos0, pos, n0, n1, l2t, stream);
+    case 1: return launch_rows<T, 1, IL, NORM>(x, y, s, H, d, gamma, eps, pos0, pos, n0, n1, l2t, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <typename T, int PG, bool IL>
-hipError_t launch_typed(const void* x, void* y, int64_t s, int H, int d, int64_t pos0, const int64_t* pos, int n0,
-                        int n1, double l2t, hipStream_t stream) {
+hipError_t launch_general(const void* x, void* y, int64_t s, int H, int d, int64_t pos0, const int64_t* pos, int n0,
+                          int n1, double l2t, hipStream_t stream) {
   const int64_t threads = s * ((d / 2) / PG);
   const int64_t blocks = (threads + kThreads - 1) / kThreads;
   if (blocks > kMaxGrid) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((rope_kernel<T, PG, IL>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
-                     stream, static_cast<const T*>(x), static_cast<T*>(y), s, H, d, pos0, pos, n0, n1, l2t);
+  hipLaunchKernelGGL((rope_kernel<T, PG, IL>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
+                     static_cast<const T*>(x), static_cast<T*>(y), s, H, d, pos0, pos, n0, n1, l2t);
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t launch_dtype(const void* x, void* y, int64_t s, int H, int d, int64_t pos0, const int64_t* pos, int n0,
-                        int n1, double l2t, int style, hipStream_t stream) {
+hipError_t launch_rope_t(const void* x, void* y, int64_t s, int H, int d, int64_t pos0, const int64_t* pos, int n0,
+                         int n1, double l2t, int style, hipStream_t stream) {
+  const int pg = rows_pairs_per_lane(d, style, int(sizeof(T)), x, y);
+  if (pg) {
+    if (style == 1)
+      return launch_rows_pg<T, true, false>(pg, x, y, s, H, d, nullptr, 0.f, pos0, pos, n0, n1, l2t, stream);
+    return launch_rows_pg<T, false, false>(pg, x, y, s, H, d, nullptr, 0.f, pos0, pos, n0, n1, l2t, stream);
+  }
   const bool wide = ((d / 2) % 4) == 0;
   if (style == 1)
-    return wide ? launch_typed<T, 4, true>(x, y, s, H, d, pos0, pos, n0, n1, l2t, stream)
-                : launch_typed<T, 1, true>(x, y, s, H, d, pos0, pos, n0, n1, l2t, stream);
-  return wide ? launch_typed<T, 4, false>(x, y, s, H, d, pos0, pos, n0, n1, l2t, stream)
-              : launch_typed<T, 1, false>(x, y, s, H, d, pos0, pos, n0, n1, l2t, stream);
+    return wide ? launch_general<T, 4, true>(x, y, s, H, d, pos0, pos, n0, n1, l2t, stream)
+                : launch_general<T, 1, true>(x, y, s, H, d, pos0, pos, n0, n1, l2t, stream);
+  return wide ? launch_general<T, 4, false>(x, y, s, H, d, pos0, pos, n0, n1, l2t, stream)
+              : launch_general<T, 1, false>(x, y, s, H, d, pos0, pos, n0, n1, l2t, stream);
 }
 
 }  // namespace
 
+int rows_pairs_per_lane(int d, int style, int eb, const void* x, const void* y) {
+  const int half = d / 2;
+  const uintptr_t addr = reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y);
+  for (int pg : {4, 8, 2, 1}) {
+    if (half % pg != 0 || half / pg > 64) continue;
+    const uintptr_t vec = uintptr_t(pg) * (style == 1 && pg > 1 ? 2 : 1) * eb;  // bytes of one vector access
+    if (addr % vec == 0) return pg;
+  }
+  return 0;
+}
+
 hipError_t launch_rope(int dtype, const void* x, void* y, int64_t s, int H, int d, int64_t pos0,
                        double theta, int style, hipStream_t stream) {
   const double l2t = log2(theta);
-  if (dtype == 0) return launch_dtype<float>(x, y, s, H, d, pos0, nullptr, d / 2, 0, l2t, style, stream);
-  return launch_dtype<uint16_t>(x, y, s, H, d, pos0, nullptr, d / 2, 0, l2t, style, stream);
+  if (dtype == 0) return launch_rope_t<float>(x, y, s, H, d, pos0, nullptr, d / 2, 0, l2t, style, stream);
+  return launch_rope_t<uint16_t>(x, y, s, H, d, pos0, nullptr, d / 2, 0, l2t, style, stream);
 }
 
 hipError_t launch_rope_mx(int dtype, const void* x, void* y, int64_t s, int H, int d, const int64_t* pos,
                           const int* sections, double theta, int style, hipStream_t stream) {
   const double l2t = log2(theta);
   if (dtype == 0)
-    return launch_dtype<float>(x, y, s, H, d, 0, pos, sections[0], sections[1], l2t, style, stream);
-  return launch_dtype<uint16_t>(x, y, s, H, d, 0, pos, sections[0], sections[1], l2t, style, stream);
-}
-
-int norm_pairs_per_lane(int d) {
-  const int half = d / 2;
-  if (half % 4 == 0 && half / 4 <= 64) return 4;
-  if (half % 8 == 0 && half / 8 <= 64) return 8;
-  if (half % 2 == 0 && half / 2 <= 64) return 2;
-  if (half <= 64) return 1;
-  return 0;
+    return launch_rope_t<float>(x, y, s, H, d, 0, pos, sections[0], sections[1], l2t, style, stream);
+  return launch_rope_t<uint16_t>(x, y, s, H, d, 0, pos, sections[0], sections[1], l2t, style, stream);
 }
 
 hipError_t launch_qk_norm_rope(int dtype, const void* x, void* y, int64_t s, int H, int d, const float* gamma,
@@ -310,11 +402,15 @@ hipError_t launch_qk_norm_rope(int dtype, const void* x, void* y, int64_t s, int
                                int style, hipStream_t stream) {
   const double l2t = log2(theta);
   const int n0 = pos ? sections[0] : d / 2, n1 = pos ? sections[1] : 0;
-  if (dtype == 0)
-    return style == 1 ? launch_norm_pg<float, true>(x, y, s, H, d, gamma, eps, pos0, pos, n0, n1, l2t, stream)
-                      : launch_norm_pg<float, false>(x, y, s, H, d, gamma, eps, pos0, pos, n0, n1, l2t, stream);
-  return style == 1 ? launch_norm_pg<uint16_t, true>(x, y, s, H, d, gamma, eps, pos0, pos, n0, n1, l2t, stream)
-                    : launch_norm_pg<uint16_t, false>(x, y, s, H, d, gamma, eps, pos0, pos, n0, n1, l2t, stream);
+  const int pg = rows_pairs_per_lane(d, style, dtype == 0 ? 4 : 2, x, y);
+  if (dtype == 0) {
+    if (style == 1)
+      return launch_rows_pg<float, true, true>(pg, x, y, s, H, d, gamma, eps, pos0, pos, n0, n1, l2t, stream);
+    return launch_rows_pg<float, false, true>(pg, x, y, s, H, d, gamma, eps, pos0, pos, n0, n1, l2t, stream);
+  }
+  if (style == 1)
+    return launch_rows_pg<uint16_t, true, true>(pg, x, y, s, H, d, gamma, eps, pos0, pos, n0, n1, l2t, stream);
+  return launch_rows_pg<uint16_t, false, true>(pg, x, y, s, H, d, gamma, eps, pos0, pos, n0, n1, l2t, stream);
 }
 
 }  // namespace spattn

@@ -141,3 +141,27 @@ def test_wrapper_and_unsupported_head_size():
     with pytest.raises(ValueError):
         sp.qk_norm_rope(x[..., :128].contiguous(), torch.ones(128, device="cuda"), pos=torch.zeros(4, 3,
                         dtype=torch.int64, device="cuda"))          # sections missing
+
+
+@pytest.mark.parametrize("style", ["half", "interleaved"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d,offset", [(128, 1), (128, 2), (64, 1)])
+def test_qk_norm_rope_unaligned_buffers(style, dtype, d, offset):
+    """Buffers starting a few elements into an allocation take narrower vector accesses (fewer
+    pairs per lane, so the row's sum of squares is added in another order): within the bars of
+    the oracle, like the aligned call."""
+    s, H = 21, 6
+    x = gen_tensor(seed=d + offset, tensor_id=1, S=s, H=H, d=d, dtype=dtype)
+    xd = to_dev(x, dtype)
+    g = torch.from_numpy(gen_gamma(3, d)).cuda()
+    n = s * H * d
+    src = torch.empty(n + offset, dtype=xd.dtype, device="cuda")[offset:].view(s, H, d)
+    src.copy_(xd)
+    out = torch.empty(n + offset, dtype=xd.dtype, device="cuda")[offset:].view(s, H, d)
+    sp.qk_norm_rope(src, g, 1e-6, 99, style=style, out=out)
+    aligned = sp.qk_norm_rope(xd, g, 1e-6, 99, style=style, out=torch.empty_like(xd))
+    torch.cuda.synchronize()
+    ref = oracle.qk_norm_rope(to_f64(x), gen_gamma(3, d).astype(np.float64), 1e-6, pos0=99, style=style)
+    _check(to_f64(aligned), ref, dtype)
+    _check(to_f64(out), oracle.qk_norm_rope(to_f64(x), gen_gamma(3, d).astype(np.float64), 1e-6, pos0=99,
+                                            style=style), dtype)

@@ -73,3 +73,25 @@ def test_rope_empty_is_noop():
     x = torch.zeros(0, 2, 8, device="cuda", dtype=torch.bfloat16)
     sp.rope_apply(x, 5)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("style", ["half", "interleaved"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d,offset", [(128, 1), (128, 2), (130, 0), (256, 1), (1024, 0), (24, 3)])
+def test_rope_layouts_and_alignments_vs_oracle(style, dtype, d, offset):
+    """Buffers that start `offset` elements into an allocation (narrower vector accesses or the
+    element-wise kernel) and head sizes whose rows do not fit one wave in groups of 1, 2, 4 or 8
+    pairs (d = 130) give the same results as the aligned case, within the RoPE bars."""
+    s, H, pos0 = 37, 5, 366000
+    x = gen_tensor(seed=d + offset, tensor_id=0, S=s, H=H, d=d, dtype=dtype)
+    xd = to_dev(x, dtype)
+    n = s * H * d
+    buf = torch.empty(n + offset, dtype=xd.dtype, device="cuda")
+    src = buf[offset:].view(s, H, d)
+    src.copy_(xd)
+    out = torch.empty(n + offset, dtype=xd.dtype, device="cuda")[offset:].view(s, H, d)
+    sp.rope_apply(src, pos0, style=style, out=out)
+    aligned = sp.rope_apply(xd, pos0, style=style, out=torch.empty_like(xd))
+    torch.cuda.synchronize()
+    _check(to_f64(out), oracle.rope_apply(to_f64(x), pos0, style=style), dtype)
+    assert to_host_bits(out).tobytes() == to_host_bits(aligned).tobytes()
