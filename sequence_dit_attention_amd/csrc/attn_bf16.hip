@@ -81,7 +81,9 @@ constexpr int kRA = SPATTN_RA;
 #ifndef SPATTN_LEAD
 #define SPATTN_LEAD 1
 #endif
-constexpr int kLead = SPATTN_LEAD;     // K/V tiles in flight ahead of the tile being used
+#ifndef SPATTN_LEAD512
+#define SPATTN_LEAD512 1
+#endif
 #ifndef SPATTN_BN
 #define SPATTN_BN 64
 #endif
@@ -122,12 +124,12 @@ struct Geo {
   // t+2 .. t+1+kLead loading.  V: tile t read, t+1 .. t+kLead loading.  Slot
   // counts are rounded up to powers of two (slot indices become masks) when
   // that still fits the 160 KiB of LDS.
+  static constexpr int kLead = D <= 128 ? SPATTN_LEAD : SPATTN_LEAD512;  // K/V tiles in flight ahead of the one in use
   static constexpr int kKNeed = kLead + (kSteps >= 2 ? 2 : 1);
   static constexpr int kVNeed = kLead + 1;
   static constexpr bool kPow2 = pow2_ceil(kKNeed) * kTileB + pow2_ceil(kVNeed) * kVTileB <= 160 * 1024;
   static constexpr int kKSlots = kPow2 ? pow2_ceil(kKNeed) : kKNeed;
   static constexpr int kVSlots = kPow2 ? pow2_ceil(kVNeed) : kVNeed;
-  static_assert(kKSlots * kTileB + kVSlots * kVTileB <= 160 * 1024, "K/V slots exceed the LDS");
   // K rows: chunk c of row r lives at c ^ (r mod kCh): the 32 rows an MFMA
   // operand read touches land on distinct chunk columns.
   static __device__ int swz_k(int r) { return r & (kCh - 1); }
@@ -534,8 +536,9 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const uint16_t* __r
                                                              int nsplit, float* __restrict__ opart) {
   using G = Geo<D, DV>;
   constexpr int QB = G::QB, BM = G::BM, kBN = G::kBN, kSteps = G::kSteps;
-  constexpr int kKSlots = G::kKSlots, kVSlots = G::kVSlots;
+  constexpr int kKSlots = G::kKSlots, kVSlots = G::kVSlots, kLead = G::kLead;
   constexpr int kNCB = D / DV;  // output column blocks per head
+  static_assert(kKSlots * G::kTileB + kVSlots * G::kVTileB <= 160 * 1024, "K/V slots exceed the LDS");
   // K tile j lives in slot j mod kKSlots, V tile j in slot j mod kVSlots.
   __shared__ __attribute__((aligned(1024))) char smem[kKSlots * G::kTileB + kVSlots * G::kVTileB];
   char* const vbase = smem + kKSlots * G::kTileB;
