@@ -66,7 +66,7 @@ bool blocks_disjoint(int32_t W, const int64_t* displs, const std::vector<int64_t
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 int launch_copies(const std::vector<CopySeg>& segs, int64_t outer, void* stream) {
-  if (segs.empty() || outer == 0) return ok();
+  if (segs.empty()) return ok();
   (void)hipGetLastError();  // launches below report their own status
   hipError_t e = spattn::launch_segcopy(segs.data(), static_cast<int>(segs.size()), outer,
                                         as_stream(stream));
@@ -293,8 +293,8 @@ namespace {
 
 // Copies between a channels-last raster [Hh, Ww, C] and its pr*pc blocks laid
 // out one after another in block order (each block row-major).  One segment
-// per block, one outer step per block row: blocks of one block row share
-// their height, so each block row is one batch of copies.
+// per block with one outer step per pixel row of the block, all blocks in one
+// batch of copies.
 int tile_copy(const char* fn, bool to_flat, int32_t dtype, const void* raster, void* raster_out, int64_t Hh,
               int64_t Ww, int64_t C, int32_t pr, int32_t pc, const void* flat_in, void* flat_out,
               int64_t flat_elems, void* stream) {
@@ -313,23 +313,24 @@ int tile_copy(const char* fn, bool to_flat, int32_t dtype, const void* raster, v
   if (!rp || !fp) return fail(SP_EINVAL, "%s: null device pointer", fn);
   if (ranges_overlap(rp, bytes, fp, bytes)) return fail(SP_EOVERLAP, "%s: raster and flat overlap", fn);
   const int64_t rowpitch = Ww * C * eb;  // bytes per raster row
-  int64_t off = 0;                       // element offset of the current block in flat
+  std::vector<CopySeg> segs;
+  int64_t off = 0;  // element offset of the current block in flat
   for (int32_t i = 0; i < pr; ++i) {
     const __int128 h = Hh, w = Ww;
     const int64_t r0 = static_cast<int64_t>((h * i) / pr), r1 = static_cast<int64_t>((h * (i + 1)) / pr);
-    std::vector<CopySeg> segs;
     for (int32_t j = 0; j < pc; ++j) {
       const int64_t c0 = static_cast<int64_t>((w * j) / pc), c1 = static_cast<int64_t>((w * (j + 1)) / pc);
       const int64_t bw = (c1 - c0) * C * eb;  // bytes per block row
       char* fl = static_cast<char*>(const_cast<void*>(fp)) + off * eb;
       char* ra = static_cast<char*>(const_cast<void*>(rp)) + r0 * rowpitch + c0 * C * eb;
-      if (to_flat) segs.push_back(CopySeg{ra, fl, bw, rowpitch, bw});
-      else segs.push_back(CopySeg{fl, ra, bw, bw, rowpitch});
+      if (to_flat) segs.push_back(CopySeg{ra, fl, bw, rowpitch, bw, r1 - r0});
+      else segs.push_back(CopySeg{fl, ra, bw, bw, rowpitch, r1 - r0});
       off += (r1 - r0) * (c1 - c0) * C;
     }
-    const int rc = launch_copies(segs, r1 - r0, stream);
-    if (rc != SP_OK) return rc;
   }
+  // one segment per block, each with its own number of pixel rows
+  const int rc = launch_copies(segs, 0, stream);
+  if (rc != SP_OK) return rc;
   return ok();
 }
 

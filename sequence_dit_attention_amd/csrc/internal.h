@@ -15,9 +15,12 @@ struct CopySeg {
   int64_t nbytes;
   int64_t src_stride;
   int64_t dst_stride;
+  int64_t outer = -1;  // outer steps of this segment; -1: the launch's `outer`
 };
 
-// Enqueue the copies of `n` segments (any n >= 0) on `stream`.
+// Enqueue the copies of `n` segments (any n >= 0) on `stream`: segment i
+// copies nbytes from src + o*src_stride to dst + o*dst_stride for each outer
+// step o below its own outer count (or the call's `outer`).
 hipError_t launch_segcopy(const CopySeg* segs, int n, int64_t outer, hipStream_t stream);
 
 // RoPE of x[s, H, d] into y (may alias x).  dtype: 0 f32, 1 bf16.  style: 0 half, 1 interleaved.

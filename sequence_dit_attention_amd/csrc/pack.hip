@@ -26,6 +26,7 @@ struct SegArgs {
   int64_t nbytes[kMaxSegs];
   int64_t src_stride[kMaxSegs];
   int64_t dst_stride[kMaxSegs];
+  int64_t outer[kMaxSegs];          // outer steps of each segment
   int64_t first_blk[kMaxSegs + 1];  // work-group prefix of each segment within one outer slice
   int nseg;
 };
@@ -37,6 +38,7 @@ __global__ __launch_bounds__(kThreads) void segcopy_kernel(SegArgs a, int64_t o_
   int s = 0;
   while (s + 1 < a.nseg && a.first_blk[s + 1] <= blk) ++s;
   const int64_t o = o_base + blockIdx.y;
+  if (o >= a.outer[s]) return;  // a segment with fewer outer steps than the launch
   const int64_t off = (blk - a.first_blk[s]) * kChunk;
   const int64_t n = min(kChunk, a.nbytes[s] - off);
   const char* src = a.src[s] + o * a.src_stride[s] + off;
@@ -75,7 +77,7 @@ hipError_t launch_segcopy(const CopySeg* segs, int n, int64_t outer, hipStream_t
   for (int base = 0; base < n; base += kMaxSegs) {
     SegArgs a{};
     a.nseg = 0;
-    int64_t blocks = 0;
+    int64_t blocks = 0, outer_max = 0;
     for (int i = base; i < n && a.nseg < kMaxSegs; ++i) {
       if (segs[i].nbytes <= 0) continue;
       const int j = a.nseg++;
@@ -84,6 +86,8 @@ hipError_t launch_segcopy(const CopySeg* segs, int n, int64_t outer, hipStream_t
       a.nbytes[j] = segs[i].nbytes;
       a.src_stride[j] = segs[i].src_stride;
       a.dst_stride[j] = segs[i].dst_stride;
+      a.outer[j] = segs[i].outer >= 0 ? segs[i].outer : outer;
+      outer_max = max(outer_max, a.outer[j]);
       a.first_blk[j] = blocks;
       blocks += (segs[i].nbytes + kChunk - 1) / kChunk;
     }
@@ -91,8 +95,8 @@ hipError_t launch_segcopy(const CopySeg* segs, int n, int64_t outer, hipStream_t
     if (a.nseg == 0) continue;
     // Grid x covers one outer slice; a segment beyond 2^31 chunks is not reachable
     // (2^31 * 4 KiB = 8 TiB), so blocks always fits.
-    for (int64_t o = 0; o < outer; o += kMaxGridY) {
-      const unsigned gy = static_cast<unsigned>(min(kMaxGridY, outer - o));
+    for (int64_t o = 0; o < outer_max; o += kMaxGridY) {
+      const unsigned gy = static_cast<unsigned>(min(kMaxGridY, outer_max - o));
       hipLaunchKernelGGL(segcopy_kernel, dim3(static_cast<unsigned>(blocks), gy), dim3(kThreads), 0,
                          stream, a, o);
       hipError_t e = hipGetLastError();
