@@ -23,13 +23,17 @@
 //    which the S^T accumulator holds them); V is read in the same order, so
 //    the contraction is unchanged.
 //  * Online softmax in float32, base 2, scale folded into log2(e).  The
-//    running maximum is only raised when a tile's maximum exceeds it by more
-//    than kTau (a factor 2^8): probabilities then stay <= 2^8, harmless in
-//    float32 sums and bf16 operands, and the O rescale (a wave-uniform
-//    branch) runs a handful of times per row instead of every tile.  The
-//    result O = sum(p v) / sum(p) does not depend on the reference maximum.
-//    Row sums add the bf16 probabilities the P*V product uses (v_dot2 with
-//    ones), so O is normalised by exactly the weights it was built from.
+//    reference maximum starts at the first block's maximum and is only raised
+//    when a block would hold a probability above 2^kTau: probabilities then
+//    stay <= 2^8, harmless in float32 sums and bf16 operands.  Instead of a
+//    maximum per block, the probabilities are computed against the current
+//    reference and a lane's block sum (needed anyway) is compared with 2^kTau
+//    before the block enters P*V; only when that check fires (a handful of
+//    times per row) is the block's maximum taken, O rescaled and the block
+//    redone.  The result O = sum(p v) / sum(p) does not depend on the
+//    reference.  Row sums add the bf16 probabilities the P*V product uses
+//    (v_dot2 with ones), so O is normalised by exactly the weights it was
+//    built from.
 //  * Software pipeline: while the softmax of tile t runs on the VALU, the
 //    MFMAs already compute S^T of tile t+1 (independent registers), then P*V
 //    of tile t follows.  The loop is unrolled by two so the two S^T register
@@ -89,6 +93,7 @@ constexpr int kRA = SPATTN_RA;
 #endif
 constexpr int pow2_ceil(int x) { return x <= 1 ? 1 : 2 * pow2_ceil((x + 1) / 2); }
 constexpr float kTau = 8.0f;           // lazy-rescale threshold (log2 units)
+constexpr float kCheck = 256.0f;       // 2^kTau: a lane's block sum above it triggers the reference check
 constexpr float kLn2 = 0.69314718055994531f;
 
 // Shape of the kernel for head size D.  D <= 128: two 32-query blocks per
@@ -286,10 +291,7 @@ __device__ inline f32x16 tail_init(int key0, int skv, int hf) {
 template <int QB>
 struct SoftState {
   float m_run[QB];  // reference maximum (log2 units) the probabilities are taken against
-  float thr[QB];    // raw-score threshold (m_run + kTau) / c above which the reference is raised
   float l_run[QB];  // this lane's partial sum of bf16 probabilities
-  float alpha[QB];  // factor taking the accumulators from the previous to the current reference
-  bool any;         // some column's reference moved: O and l must be scaled by alpha
 };
 
 // max(a, b, c) in one instruction (the compiler would otherwise build a
@@ -300,43 +302,17 @@ __device__ inline float max3(float a, float b, float c) {
   return r;
 }
 
-// Reference update after the block maxima mx (raw scores, per lane: the
-// lane's 16 keys of its query column) are known.  The common case is one
-// compare per query block and a ballot.  Only when some lane's maximum
-// exceeds its column's threshold are the two wave halves combined and the
-// columns whose maximum really exceeds the reference by more than kTau
-// raised; every other column keeps its reference (alpha = 1 exactly), so a
-// row's arithmetic never depends on the other rows of the wave.
+// Maximum of a 32-key block per query column (raw scores; the lane's 16
+// keys, then the other wave half), in log2 units.
 template <int QB>
-__device__ inline void update_ref(const float (&mx)[QB], SoftState<QB>& st, float c) {
-  bool need = false;
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) need |= mx[qb] > st.thr[qb];
-  st.any = __builtin_amdgcn_ballot_w64(need) != 0;
-  if (st.any) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float mt = other_half_max(mx[qb]) * c;
-      const float m_new = mt > st.m_run[qb] + kTau ? mt : st.m_run[qb];
-      st.alpha[qb] = __builtin_amdgcn_exp2f(st.m_run[qb] - m_new);
-      st.m_run[qb] = m_new;
-      st.thr[qb] = (m_new + kTau) * __builtin_amdgcn_rcpf(c);
-    }
-  }
-}
-
-// Maximum of a 32-key block, then the reference update.
-template <int QB>
-__device__ inline void block_max(const f32x16 (&s)[QB], SoftState<QB>& st, float c) {
-  float mx[QB];
+__device__ inline void block_max(const f32x16 (&s)[QB], float (&mt)[QB], float c) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     float m = fmaxf(s[qb][0], s[qb][1]);
 #pragma unroll
     for (int r = 2; r < 16; r += 2) m = max3(m, s[qb][r], s[qb][r + 1]);
-    mx[qb] = m;
+    mt[qb] = other_half_max(m) * c;
   }
-  update_ref(mx, st, c);
 }
 
 // Probabilities of a 32-key block as packed bf16 pairs: pw[qb][u][e] holds
@@ -362,11 +338,11 @@ __device__ inline void rescale_o(f32x16 (&o)[G::kND][QB], const float (&alpha)[Q
 // for 8 passes while the following VALU instructions issue), and LDS operand
 // reads are issued two MFMA pairs ahead of their use.
 //
-// On entry `cur` holds S^T of the step's keys and `st` its reference maximum.
+// On entry `cur` holds S^T of the step's keys and `st` the reference maximum.
 // Part A: MFMAs compute S^T of the next 32 keys into `nxt` (HAS_NEXT) while the
-//         VALU turns `cur` into bf16 probabilities (fma, exp2, cvt).
-// Part B: MFMAs accumulate P*V while the VALU adds the row sums (v_dot2) and
-//         takes the maximum of `nxt`.
+//         VALU turns `cur` into bf16 probabilities (fma, exp2, cvt) and adds
+//         their row sums (v_dot2); then the block check (see above).
+// Part B: MFMAs accumulate P*V.
 template <int D>
 __device__ inline bf16x8 k_frag(const char* kb, int r0, int cc, int col, int hf) {
   using G = Geo<D>;
@@ -395,11 +371,6 @@ __device__ __attribute__((always_inline)) inline void step32(f32x16 (&cur)[QB], 
   constexpr int kB = 2 * QB * G::kND;  // MFMA slots of part B: P*V
   constexpr int kNV = 2 * G::kND;      // V^T fragments (MFMA pairs u, db) per step
   static_assert(kA >= 2 * kRA && kB >= 2 * kRA, "prefetch slots");
-  if (st.any) {  // reference raised at the end of the previous step
-    rescale_o<G>(acc, st.alpha);
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) st.l_run[qb] *= st.alpha[qb];
-  }
   __builtin_amdgcn_sched_barrier(0);
 
   // V^T fragment reads (issued from the end of part A on)
@@ -415,17 +386,15 @@ __device__ __attribute__((always_inline)) inline void step32(f32x16 (&cur)[QB], 
     const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p1);
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  float mx[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) mx[qb] = -INFINITY;
   bf16x8 vf[kNV];
 
   // ---- part A: MFMA slot i computes (cc = i / QB, qb = i % QB) of S^T(next);
-  // the VALU produces the bf16 probability words of `cur` and their row sums.
+  // the VALU produces the bf16 probability words of `cur` and the block's
+  // row sums.
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   float ls[QB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) ls[qb] = st.l_run[qb];
+  for (int qb = 0; qb < QB; ++qb) ls[qb] = 0.f;
   const int rk = rk_next + col;
   const char* krow = kb_next + rk * G::kRowB;
   const int ksw = G::swz_k(rk);
@@ -463,15 +432,49 @@ __device__ __attribute__((always_inline)) inline void step32(f32x16 (&cur)[QB], 
     __builtin_amdgcn_sched_barrier(0);
   }
   // Keep the row sums in part A: an empty asm consuming them stops IR passes
-  // from sinking the v_dot2 chain past the fences into the next step.
+  // from sinking the v_dot2 chain past the fences.
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    asm volatile("" : "+v"(ls[qb]));
-    st.l_run[qb] = ls[qb];
-  }
+  for (int qb = 0; qb < QB; ++qb) asm volatile("" : "+v"(ls[qb]));
 
-  // ---- part B: MFMA slot i accumulates pair k = i / QB (u, db) for qb = i % QB;
-  // the VALU takes the maximum of the next block.
+  // ---- check before the block enters P*V: every probability is at most
+  // 2^kTau unless some lane's sum over its 16 keys exceeds 2^kTau (an
+  // overflow to inf included).  Rarely, when it does, the block's maximum is
+  // taken, the reference of the columns whose maximum exceeds it by more than
+  // kTau is raised (the others keep it, alpha = 1 exactly, so no row depends
+  // on the other rows of the wave), O and l are rescaled and the block's
+  // words redone from the scores, which are still in registers.
+  {
+    bool need = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) need |= ls[qb] > kCheck;
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      float mt[QB], alpha[QB];
+      block_max(cur, mt, c);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float m_new = mt[qb] > st.m_run[qb] + kTau ? mt[qb] : st.m_run[qb];
+        alpha[qb] = __builtin_amdgcn_exp2f(st.m_run[qb] - m_new);
+        st.m_run[qb] = m_new;
+        st.l_run[qb] *= alpha[qb];
+        ls[qb] = 0.f;
+      }
+      rescale_o<G>(acc, alpha);
+#pragma unroll
+      for (int w = 0; w < 8 * QB; ++w) {
+        const int pq = w >> 3, pr = w & 7;
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(cur[pq][2 * pr], c, -st.m_run[pq]));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(cur[pq][2 * pr + 1], c, -st.m_run[pq]));
+        const uint32_t word = pack_bf16x2(p0, p1);
+        pb[pq][pr >> 2][pr & 3] = word;
+        ls[pq] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, word), ones, ls[pq], false);
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) st.l_run[qb] += ls[qb];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- part B: MFMA slot i accumulates pair k = i / QB (u, db) for qb = i % QB.
 #pragma unroll
   for (int i = 0; i < kB; ++i) {
     const int k = i / QB, qb = i % QB;
@@ -480,17 +483,11 @@ __device__ __attribute__((always_inline)) inline void step32(f32x16 (&cur)[QB], 
     acc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
         vf[k], __builtin_bit_cast(bf16x8, u32x4{pb[qb][u][0], pb[qb][u][1], pb[qb][u][2], pb[qb][u][3]}),
         acc[db][qb], 0, 0, 0);
-    if (HAS_NEXT)
-      slot_items<8 * QB, kB>(i, [&](int w) {
-        const int xq = w >> 3, xr = w & 7;
-        mx[xq] = max3(mx[xq], nxt[xq][2 * xr], nxt[xq][2 * xr + 1]);
-      });
 #pragma unroll
     for (int r = 0; r < kRA; ++r)
       if (PRE_NEXT && i == kB - 2 * kRA + r) kpre[r] = k_frag<D>(kb_after, rk_after, r, col, hf);
     __builtin_amdgcn_sched_barrier(0);
   }
-  if (HAS_NEXT) update_ref(mx, st, c);
 }
 
 // f(integral_constant<int, I>) for I = 0, 1, ...: a loop whose index is a
@@ -671,12 +668,7 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const uint16_t* __r
       for (int r = 0; r < 16; ++r) acc[db][qb][r] = 0.f;
   SoftState<QB> st;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    st.m_run[qb] = -INFINITY;
-    st.thr[qb] = -INFINITY;
-    st.l_run[qb] = 0.f;
-    st.alpha[qb] = 1.f;
-  }
+  for (int qb = 0; qb < QB; ++qb) st.l_run[qb] = 0.f;
   const f32x16 zero = {};
 
   f32x16 sa[QB], sb[QB];  // S^T of the current / next 32 keys
@@ -685,7 +677,7 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const uint16_t* __r
   tile_barrier<0>();
   if (nT == 1) qk32<D, true>(sa, kslot(0), 0, qf, tail_init(0, skv, hf), col, hf);
   else qk32<D, false>(sa, kslot(0), 0, qf, zero, col, hf);
-  block_max(sa, st, c);
+  block_max(sa, st.m_run, c);  // the first block's maximum is the first reference (every column has a key)
   // K fragments of the next step's part A are read ahead, at the end of the
   // previous part B (that K tile has been resident since an earlier barrier).
   bf16x8 kpre[kRA];
