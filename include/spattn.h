@@ -9,16 +9,22 @@
  * sequence with AllGatherV semantics (per-rank element counts and
  * displacements into one flat buffer, then narrow/view/concat), attention runs
  * with the rank's local queries against the full K/V, and the per-rank outputs
- * are concatenated back along the sequence.
+ * are concatenated back along the sequence.  Page "NPU HunyuanImage-3.0模型推理
+ * 优化实践" adds the per-head norm in front of the rotation (section 计算分解)
+ * and the VAE's spatial block split (section VAE并行优化), whose attention
+ * gathers the K/V of all blocks the same way.
  *
  * Conventions shared by every entry point
- *  - Tensors are dense, contiguous and token-major: [tokens, H, d] (batch 1).
+ *  - Tensors are dense, contiguous and token-major: [tokens, H, d] (batch 1);
+ *    a VAE feature map is channels-last [Hh, Ww, C], i.e. Hh*Ww tokens of one
+ *    head of C channels.
  *  - Element types: SP_F32 (IEEE binary32) or SP_BF16 (bfloat16 bit patterns).
  *  - Counts, displacements and lengths are in ELEMENTS, as in AllGatherV.
  *  - Device pointers are HIP device memory of the current device; host arrays
  *    are read during the call only.  The caller allocates and frees every
  *    buffer; the library keeps no pointer after a call returns and makes no
- *    device allocation.
+ *    device allocation (scratch memory, where a call needs it, is a
+ *    caller-owned workspace argument).
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
  *    is enqueued asynchronously on it; nothing synchronises with the host.
  *    The caller synchronises the stream before reading results, as the
