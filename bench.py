@@ -88,7 +88,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="p768_15s_w4")
-    ap.add_argument("--cpu-rows", type=int, default=192, help="query rows in the CPU-oracle sample (0: skip)")
+    ap.add_argument("--cpu-rows", type=int, default=400,
+                    help="query rows in the CPU-oracle sample, about 10-15 s of host work (0: skip)")
     ap.add_argument("--vae-steps", type=int, default=3, help="timed steps of the VAE block-split share (0: skip)")
     ap.add_argument("--gf-steps", type=int, default=2,
                     help="steps of the gather-free variant timed after the headline steps (0: skip)")
