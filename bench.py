@@ -77,9 +77,33 @@ def cpu_baseline(wl, q, k, v, a, b, rows: int):
         oracle.attention(qrows[:, h:h + 1, :], kh, vh)
         spent += time.perf_counter() - t0
     flops = 4.0 * rows * wl.S * wl.H * wl.d
+
+    # The data-movement rows beside it: the oracle's AllGatherV pack of the four
+    # K shards (the whole tensor, bf16 bit patterns) and its RoPE on 2,048
+    # tokens of the rank's Q slice (float64), as algorithmic GB/s of the bf16 data.
+    bounds = [oracle.shard_bounds(wl.S, wl.W, r) for r in range(wl.W)]
+    inner = wl.H * wl.d
+    counts, displs = oracle.allgatherv_layout(wl.S, wl.W, 1, inner)
+    sends = [np.ascontiguousarray(k[x:y]).reshape(-1) for x, y in bounds]
+    flat = np.empty(wl.S * inner, dtype=k.dtype)
+    t0 = time.perf_counter()
+    oracle.varlen_pack(sends, counts, displs, flat)
+    t_pack = time.perf_counter() - t0
+    nr = min(2048, b - a)
+    qs = bf16_bits_to_f32(q[a:a + nr]).astype(np.float64)
+    t0 = time.perf_counter()
+    oracle.rope_apply(qs, a, wl.theta)
+    t_rope = time.perf_counter() - t0
+    pack_b = 2.0 * wl.S * inner * k.itemsize
+    rope_b = 2.0 * nr * inner * 2
     return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{rows} query rows x {wl.H} heads of the rank-{wl.ranks[0]} shard against the full "
-                      f"{wl.S}-token K/V (fp64 numpy oracle attention, {spent:.1f} s)"}
+                      f"{wl.S}-token K/V (fp64 numpy oracle attention, {spent:.1f} s)",
+            "other_rows": {
+                "pack_kv_gbs": pack_b / t_pack / 1e9,
+                "pack_sample": f"the {wl.W} K shards ({pack_b / 2e9:.2f} GB of bf16) into one flat buffer, {t_pack:.2f} s",
+                "rope_gbs": rope_b / t_rope / 1e9,
+                "rope_sample": f"{nr} tokens x {wl.H} heads of the rank's Q slice in float64, {t_rope:.2f} s"}}
 
 
 def main() -> int:
