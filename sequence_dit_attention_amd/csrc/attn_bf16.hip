@@ -731,11 +731,29 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const uint16_t* __r
   uint64_t kaddr = reinterpret_cast<uint64_t>(kh) + uint64_t(kLead + 1) * tb;
   uint64_t vaddr = reinterpret_cast<uint64_t>(vh) + uint64_t(kLead) * tb;
   int t = 0;
+  // Sharded K/V: tiles below kcross (vcross) lie inside the stream's current
+  // shard and advance from kaddr (vaddr) like gathered ones; a tile at or
+  // past it goes through the cursor, which also resets the address and the
+  // crossing point.
+  int kcross = 0, vcross = 0;
   for (; t <= nT - 3 - kLead; ++t) {
     tile_barrier<kBatch * (kLead - 1)>();
     if constexpr (GV) {
-      load_sharded(kl, kv.k, kcur, t + kLead + 1, kslot(t + kLead + 1));
-      load_sharded(vl, kv.v, vcur, t + kLead, vslot(t + kLead));
+      const int jk = t + kLead + 1, jv = t + kLead;
+      if (jk >= kcross) {
+        load_sharded(kl, kv.k, kcur, jk, kslot(jk));
+        kaddr = reinterpret_cast<uint64_t>(kcur.p) + uint64_t(int64_t(jk) * kBN - kcur.s0) * uint64_t(rowbytes);
+        kcross = kcur.s1 / kBN;
+      } else {
+        kl.load_at(kaddr, kslot(jk), wave);
+      }
+      if (jv >= vcross) {
+        load_sharded(vl, kv.v, vcur, jv, vslot(jv));
+        vaddr = reinterpret_cast<uint64_t>(vcur.p) + uint64_t(int64_t(jv) * kBN - vcur.s0) * uint64_t(rowbytes);
+        vcross = vcur.s1 / kBN;
+      } else {
+        vl.load_at(vaddr, vslot(jv), wave);
+      }
     } else {
       kl.load_at(kaddr, kslot(t + kLead + 1), wave);
       vl.load_at(vaddr, vslot(t + kLead), wave);
