@@ -75,3 +75,25 @@ def test_vae_128x128_block_sampled_rows():
     ro, _ = oracle.attention_rows(widen(qb[rows]), k, v, widen=widen)   # raster-order keys
     err, rel = attn_errors(to_f64(o)[rows], ro)
     assert err <= 2e-2 and rel <= 1e-2, (err, rel)
+
+
+def test_split_at_the_768p_5s_rank_share_sampled_rows():
+    """Rank 3 of the 768P/5 s workload (31,280 queries x 125,117 keys x 24 heads of 128) with 3 key ranges:
+    32 sampled query rows x all heads against the oracle, and the whole output within the bf16 bars of the
+    plain call."""
+    S, W, H, d = 125117, 4, 24, 128
+    a, b = sp.sp_shard_bounds(S, W, 3)
+    q = gen_tensor(4, 0, S, H, d, "bf16", tok0=a, tok1=b)
+    k = gen_tensor(4, 1, S, H, d, "bf16")
+    v = gen_tensor(4, 2, S, H, d, "bf16")
+    qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    o_split = sp.shard_attn_fwd_split(qd, kd, vd, 3)
+    o_plain = sp.shard_attn_fwd(qd, kd, vd)
+    torch.cuda.synchronize()
+    rows = sample_rows(b - a, 32, seed=6)
+    widen = lambda x: bf16_bits_to_f32(x).astype(np.float64)
+    ro, _ = oracle.attention_rows(widen(q[rows]), k, v, widen=widen)
+    err, rel = attn_errors(to_f64(o_split)[rows], ro)
+    assert err <= 2e-2 and rel <= 1e-2, (err, rel)
+    d_all = (o_split.float() - o_plain.float()).abs().max().item()
+    assert d_all <= 2e-2 and d_all <= 1e-2 * o_plain.float().abs().max().item(), d_all
