@@ -85,6 +85,12 @@ constexpr int kRA = SPATTN_RA;
 #ifndef SPATTN_LEAD
 #define SPATTN_LEAD 1
 #endif
+#ifndef SPATTN_EOFF
+#define SPATTN_EOFF 2
+#endif
+#ifndef SPATTN_EARLY
+#define SPATTN_EARLY 4
+#endif
 #ifndef SPATTN_LEAD512
 #define SPATTN_LEAD512 1
 #endif
@@ -111,6 +117,9 @@ struct Geo {
   static constexpr int kBN = D <= 128 ? SPATTN_BN : 32;   // keys per tile
   static constexpr int kSteps = kBN / 32;                 // 32-key steps per tile
   static_assert(kSteps == 1 || kSteps % 2 == 0, "the two S^T register sets alternate within a tile");
+  // Probability words per query block made one step early, under the P*V
+  // MFMAs of the previous step (the part of a step that has no other VALU work).
+  static constexpr int kEarly = D <= 128 ? SPATTN_EARLY : 0;
   // With two or more steps per tile, the first K fragments of the block after
   // next are read ahead at the end of a step; with one step that block is two
   // tiles ahead and the fragments are read at the start of the step instead.
@@ -342,7 +351,11 @@ __device__ inline void rescale_o(f32x16 (&o)[G::kND][QB], const float (&alpha)[Q
 // Part A: MFMAs compute S^T of the next 32 keys into `nxt` (HAS_NEXT) while the
 //         VALU turns `cur` into bf16 probabilities (fma, exp2, cvt) and adds
 //         their row sums (v_dot2); then the block check (see above).
-// Part B: MFMAs accumulate P*V.
+// Part B: MFMAs accumulate P*V while the VALU makes the first kEarly
+//         probability words of `nxt` (HAS_NEXT), so that both parts carry
+//         about the same vector work.  Those words and their row sums enter
+//         the next step in `pbn` / `ln`; if that step's check raises the
+//         reference, all of its words are made again.
 template <int D>
 __device__ inline bf16x8 k_frag(const char* kb, int r0, int cc, int col, int hf) {
   using G = Geo<D>;
@@ -359,9 +372,23 @@ __device__ inline void slot_items(int i, F&& f) {
     if (w * M / N == i) f(w);
 }
 
+// Probability word pr of query block pq: exp2(c*s - m) of scores 2pr, 2pr+1,
+// rounded to bf16 and packed, its two values added to the row sum ls.
+template <int QB>
+__device__ __attribute__((always_inline)) inline void prob_word(const f32x16 (&s)[QB], const SoftState<QB>& st,
+                                                               float c, int pq, int pr, PW<QB>& pb,
+                                                               float (&ls)[QB]) {
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  const float p0 = __builtin_amdgcn_exp2f(fmaf(s[pq][2 * pr], c, -st.m_run[pq]));
+  const float p1 = __builtin_amdgcn_exp2f(fmaf(s[pq][2 * pr + 1], c, -st.m_run[pq]));
+  const uint32_t word = pack_bf16x2(p0, p1);
+  pb[pq][pr >> 2][pr & 3] = word;
+  ls[pq] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, word), ones, ls[pq], false);
+}
+
 template <typename G, bool HAS_NEXT, bool MASK_NEXT, bool PRE_NEXT, int QB = G::QB>
 __device__ __attribute__((always_inline)) inline void step32(f32x16 (&cur)[QB], f32x16 (&nxt)[QB], SoftState<QB>& st,
-                              PW<QB>& pb,
+                              PW<QB>& pb, PW<QB>& pbn, float (&lc)[QB], float (&ln)[QB],
                               f32x16 (&acc)[G::kND][QB], const bf16x8 (&qf)[QB][G::kDC],
                               const char* kb_next, int rk_next, const f32x16& init_next, const char* vb, int rv,
                               float c, int lane, int col, int hf, bf16x8 (&kpre)[kRA], const char* kb_after,
@@ -370,6 +397,8 @@ __device__ __attribute__((always_inline)) inline void step32(f32x16 (&cur)[QB], 
   constexpr int kA = QB * G::kDC;      // MFMA slots of part A: S^T of the next block
   constexpr int kB = 2 * QB * G::kND;  // MFMA slots of part B: P*V
   constexpr int kNV = 2 * G::kND;      // V^T fragments (MFMA pairs u, db) per step
+  constexpr int kE = G::kEarly;        // words per query block made during the previous step's part B
+  constexpr int kEOff = SPATTN_EOFF;   // part B slots before the first early word (S^T of the next block settles)
   static_assert(kA >= 2 * kRA && kB >= 2 * kRA, "prefetch slots");
   __builtin_amdgcn_sched_barrier(0);
 
@@ -389,12 +418,11 @@ __device__ __attribute__((always_inline)) inline void step32(f32x16 (&cur)[QB], 
   bf16x8 vf[kNV];
 
   // ---- part A: MFMA slot i computes (cc = i / QB, qb = i % QB) of S^T(next);
-  // the VALU produces the bf16 probability words of `cur` and the block's
-  // row sums.
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  // the VALU produces the remaining bf16 probability words of `cur` and
+  // completes the block's row sums.
   float ls[QB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) ls[qb] = 0.f;
+  for (int qb = 0; qb < QB; ++qb) ls[qb] = lc[qb];
   const int rk = rk_next + col;
   const char* krow = kb_next + rk * G::kRowB;
   const int ksw = G::swz_k(rk);
@@ -418,13 +446,8 @@ __device__ __attribute__((always_inline)) inline void step32(f32x16 (&cur)[QB], 
       else
         nxt[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cc], qf[qb][cc], f32x16{}, 0, 0, 0);
     }
-    slot_items<8 * QB, kA>(i, [&](int w) {  // word w: query block w/8, pair w%8
-      const int pq = w >> 3, pr = w & 7;
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(cur[pq][2 * pr], c, -st.m_run[pq]));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(cur[pq][2 * pr + 1], c, -st.m_run[pq]));
-      const uint32_t word = pack_bf16x2(p0, p1);
-      pb[pq][pr >> 2][pr & 3] = word;
-      ls[pq] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, word), ones, ls[pq], false);
+    slot_items<(8 - kE) * QB, kA>(i, [&](int w) {  // the late words: query block w/(8-kE), pair kE + w%(8-kE)
+      prob_word(cur, st, c, w / (8 - kE), kE + w % (8 - kE), pb, ls);
     });
 #pragma unroll
     for (int r = 0; r < kRA; ++r)
@@ -460,21 +483,19 @@ __device__ __attribute__((always_inline)) inline void step32(f32x16 (&cur)[QB], 
       }
       rescale_o<G>(acc, alpha);
 #pragma unroll
-      for (int w = 0; w < 8 * QB; ++w) {
-        const int pq = w >> 3, pr = w & 7;
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(cur[pq][2 * pr], c, -st.m_run[pq]));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(cur[pq][2 * pr + 1], c, -st.m_run[pq]));
-        const uint32_t word = pack_bf16x2(p0, p1);
-        pb[pq][pr >> 2][pr & 3] = word;
-        ls[pq] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, word), ones, ls[pq], false);
-      }
+      for (int w = 0; w < 8 * QB; ++w) prob_word(cur, st, c, w >> 3, w & 7, pb, ls);
     }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) st.l_run[qb] += ls[qb];
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- part B: MFMA slot i accumulates pair k = i / QB (u, db) for qb = i % QB.
+  // ---- part B: MFMA slot i accumulates pair k = i / QB (u, db) for qb = i % QB,
+  // while the VALU makes the early words of the next block (its scores are
+  // complete: part A's MFMAs have been issued) under the reference that the
+  // check above has settled.
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) ln[qb] = 0.f;
 #pragma unroll
   for (int i = 0; i < kB; ++i) {
     const int k = i / QB, qb = i % QB;
@@ -486,7 +507,13 @@ __device__ __attribute__((always_inline)) inline void step32(f32x16 (&cur)[QB], 
 #pragma unroll
     for (int r = 0; r < kRA; ++r)
       if (PRE_NEXT && i == kB - 2 * kRA + r) kpre[r] = k_frag<D>(kb_after, rk_after, r, col, hf);
+    if (HAS_NEXT && i >= kEOff)
+      slot_items<kE * QB, kB - kEOff>(i - kEOff, [&](int w) { prob_word(nxt, st, c, w / kE, w % kE, pbn, ln); });
     __builtin_amdgcn_sched_barrier(0);
+  }
+  if (HAS_NEXT && kE > 0) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) asm volatile("" : "+v"(ln[qb]));
   }
 }
 
@@ -672,12 +699,19 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const uint16_t* __r
   const f32x16 zero = {};
 
   f32x16 sa[QB], sb[QB];  // S^T of the current / next 32 keys
-  PW<QB> pb;
+  PW<QB> pa, pn;          // probability words of the current / next block
+  float la[QB], ln[QB];   // row sums of the words made early
 
   tile_barrier<0>();
   if (nT == 1) qk32<D, true>(sa, kslot(0), 0, qf, tail_init(0, skv, hf), col, hf);
   else qk32<D, false>(sa, kslot(0), 0, qf, zero, col, hf);
   block_max(sa, st.m_run, c);  // the first block's maximum is the first reference (every column has a key)
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    la[qb] = 0.f;
+#pragma unroll
+    for (int pr = 0; pr < G::kEarly; ++pr) prob_word(sa, st, c, qb, pr, pa, la);
+  }
   // K fragments of the next step's part A are read ahead, at the end of the
   // previous part B (that K tile has been resident since an earlier barrier).
   bf16x8 kpre[kRA];
@@ -710,14 +744,23 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const uint16_t* __r
       const int rk_after = after_in ? 32 * (s + 2) : 32 * (s + 2 - kSteps);
       const f32x16 init = MASK_NEXT ? tail_init(t * kBN + 32 * (s + 1), skv, hf) : zero;
       if constexpr (s % 2 == 0)
-        step32<G, HAS_NEXT, MASK_NEXT, PRE_NEXT>(sa, sb, st, pb, acc, qf, kb_next, rk_next, init, vb, 32 * s, c,
+        step32<G, HAS_NEXT, MASK_NEXT, PRE_NEXT>(sa, sb, st, pa, pn, la, ln, acc, qf, kb_next, rk_next, init, vb, 32 * s, c,
                                                  lane, col, hf, kpre, kb_after, rk_after);
       else
-        step32<G, HAS_NEXT, MASK_NEXT, PRE_NEXT>(sb, sa, st, pb, acc, qf, kb_next, rk_next, init, vb, 32 * s, c,
+        step32<G, HAS_NEXT, MASK_NEXT, PRE_NEXT>(sb, sa, st, pn, pa, ln, la, acc, qf, kb_next, rk_next, init, vb, 32 * s, c,
                                                  lane, col, hf, kpre, kb_after, rk_after);
       if constexpr (kSteps == 1) {  // one step per tile: the next tile's S^T moves to the current set
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) sa[qb] = sb[qb];
+        for (int qb = 0; qb < QB; ++qb) {
+          sa[qb] = sb[qb];
+          if constexpr (G::kEarly > 0) {  // and so do the early words
+            la[qb] = ln[qb];
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) pa[qb][u][e] = pn[qb][u][e];
+          }
+        }
       }
     };
     for_each_index(std::make_integer_sequence<int, kSteps>{}, one);
