@@ -232,7 +232,7 @@ int rope_apply(int32_t dtype, const void* x, void* y, int64_t s, int32_t H, int3
   if (d < 2 || d > 1024 || (d & 1)) return fail(SP_EINVAL, "rope_apply: d must be even, 2..1024 (got %d)", d);
   if (!(std::isfinite(theta) && theta > 0.0)) return fail(SP_EINVAL, "rope_apply: theta must be finite and > 0");
   const int64_t lim = int64_t(1) << 53;
-  if (pos0 <= -lim || pos0 >= lim || pos0 + s >= lim)
+  if (pos0 <= -lim || pos0 >= lim || s >= lim || pos0 + s >= lim)
     return fail(SP_EINVAL, "rope_apply: positions must stay within +-2^53");
   int64_t n, bytes;
   if (!mul_ok(s, int64_t(H) * d, &n) || !mul_ok(n, eb, &bytes))
@@ -329,9 +329,7 @@ int tile_copy(const char* fn, bool to_flat, int32_t dtype, const void* raster, v
     }
   }
   // one segment per block, each with its own number of pixel rows
-  const int rc = launch_copies(segs, 0, stream);
-  if (rc != SP_OK) return rc;
-  return ok();
+  return launch_copies(segs, 0, stream);
 }
 
 }  // namespace
@@ -364,7 +362,7 @@ int qk_norm_rope(int32_t dtype, const void* x, void* y, int64_t s, int32_t H, in
       return fail(SP_EINVAL, "%s: sections must be >= 0 and add up to d/2 = %d pairs", fn, d / 2);
   } else {
     const int64_t lim = int64_t(1) << 53;
-    if (pos0 <= -lim || pos0 >= lim || pos0 + s >= lim)
+    if (pos0 <= -lim || pos0 >= lim || s >= lim || pos0 + s >= lim)
       return fail(SP_EINVAL, "%s: positions must stay within +-2^53", fn);
   }
   int64_t n, bytes, pbytes;

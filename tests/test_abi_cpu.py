@@ -106,6 +106,7 @@ def test_rope_validation():
     assert L.rope_apply(1, FAKE, FAKE, 10, 2, 8, 0, 1e4, 5, None) == SP_EINVAL      # style
     assert L.rope_apply(1, FAKE, FAKE, 10, 0, 8, 0, 1e4, 0, None) == SP_EINVAL      # H
     assert L.rope_apply(1, FAKE, FAKE, 10, 2, 8, 2**53, 1e4, 0, None) == SP_EINVAL  # positions
+    assert L.rope_apply(1, FAKE, FAKE, 2**62, 2, 8, 2**53 - 1, 1e4, 0, None) == SP_EINVAL  # pos0 + s, no wrap
     assert L.rope_apply(1, FAKE, FAKE + 2, 10, 2, 8, 0, 1e4, 0, None) == SP_EOVERLAP
 
 
