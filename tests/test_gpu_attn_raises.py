@@ -1,0 +1,84 @@
+"""GPU parity of the bf16 attention when the softmax reference has to rise.
+
+The kernels keep a per-row reference maximum and raise it only when a 32-key
+block holds a logit more than 8 (base 2) above it; part of a block's
+probabilities is made one step early, under the reference of the time, and is
+made again when the block's check raises it.  These inputs force that to
+happen at chosen keys: every query row leans on axis 0 (even rows) or axis 1
+(odd rows), and "spike" keys on those axes grow by about 10 (base 2) from one
+spike of an axis to the next.  The spikes sit at the first and last key of a
+block, at tile edges, in the ragged last tile and on the very last key, so
+the raise happens in the first step, in either step of a tile, in the masked
+tail and in the last step; the two axes make neighbouring columns of a wave
+raise at different blocks.  The final output is dominated by the last spike of
+the row's axis; bars as for shard_attn_fwd (bf16: 2e-2 absolute and 1e-2 of
+max |O|), checked against the float64 oracle, plus the LSE.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sequence_dit_attention_amd as sp
+from synth import f32_to_bf16_bits
+from tests._helpers import attn_errors, to_dev, to_f64, to_host_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(sq, skv, H, d, seed):
+    rng = np.random.default_rng(seed)
+    q = 0.5 * rng.standard_normal((sq, H, d))
+    k = 0.5 * rng.standard_normal((skv, H, d))
+    v = rng.standard_normal((skv, H, d))
+    q[0::2, :, 0] += 4.0
+    q[1::2, :, 1] += 4.0
+    # logit gain of one spike step on an axis: 4 * step / sqrt(d) * log2(e) ~ 10 (base 2)
+    step = 10.0 * np.sqrt(d) / (4.0 * np.log2(np.e))
+    spikes = sorted({p for p in (0, 31, 32, 33, 63, 64, 65, 127, 128, 160, skv - 40, skv - 2, skv - 1)
+                     if 0 <= p < skv})
+    for i, p in enumerate(spikes):
+        k[p, :, i % 2] += 4.0 + step * (i // 2)
+    bits = [f32_to_bf16_bits(a.astype(np.float32)) for a in (q, k, v)]
+    return bits
+
+
+def _check(o, lse, qb, kb, vb):
+    ro, rl = oracle.attention(to_f64(qb), to_f64(kb), to_f64(vb))
+    err, rel = attn_errors(to_f64(o), ro)
+    assert err <= 2e-2 and rel <= 1e-2, (err, rel)
+    assert float(np.max(np.abs(ro))) > 0.5  # dominated by spikes, not averaged out
+    if lse is not None:
+        assert np.max(np.abs(lse.cpu().numpy() - rl)) <= 2e-2
+
+
+@pytest.mark.parametrize("d", [64, 128, 512])
+@pytest.mark.parametrize("skv", [192, 1000])
+def test_reference_raises(d, skv):
+    H = 1 if d == 512 else 2
+    sq = 293
+    qb, kb, vb = _inputs(sq, skv, H, d, seed=d + skv)
+    q, k, v = (to_dev(a, "bf16") for a in (qb, kb, vb))
+    lse = torch.empty(H, sq, dtype=torch.float32, device="cuda")
+    o = sp.shard_attn_fwd(q, k, v, lse=lse)
+    torch.cuda.synchronize()
+    _check(o, lse, qb, kb, vb)
+    if d != 512:  # the shard table walks the same keys: bit-identical
+        cut = [0, 100, 500, skv] if skv > 500 else [0, 64, 65, skv]
+        ks = [k[a:b].contiguous() for a, b in zip(cut, cut[1:])]
+        vs = [v[a:b].contiguous() for a, b in zip(cut, cut[1:])]
+        o2 = sp.shard_attn_fwd_gv(q, ks, vs)
+        torch.cuda.synchronize()
+        assert to_host_bits(o2).tobytes() == to_host_bits(o).tobytes()
+
+
+@pytest.mark.parametrize("d", [128, 512])
+def test_reference_raises_split(d):
+    H = 1 if d == 512 else 2
+    sq, skv = 160, 1000
+    qb, kb, vb = _inputs(sq, skv, H, d, seed=7 + d)
+    q, k, v = (to_dev(a, "bf16") for a in (qb, kb, vb))
+    lse = torch.empty(H, sq, dtype=torch.float32, device="cuda")
+    o = sp.shard_attn_fwd_split(q, k, v, nsplit=3, lse=lse)
+    torch.cuda.synchronize()
+    _check(o, lse, qb, kb, vb)
