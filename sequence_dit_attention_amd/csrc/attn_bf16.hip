@@ -70,6 +70,9 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Build-time shape knobs.  The defaults are the configuration the library is
+// built, tested and measured with; other values compile (they were used to
+// time alternatives) but are not part of the tested product.
 #ifndef SPATTN_WAVES
 #define SPATTN_WAVES 4
 #endif
@@ -83,19 +86,19 @@ constexpr int kThreads = 64 * kWaves;
 #endif
 constexpr int kRA = SPATTN_RA;
 #ifndef SPATTN_LEAD
-#define SPATTN_LEAD 1
+#define SPATTN_LEAD 1  // K/V tiles loaded ahead of the one in use (head sizes 64, 128)
 #endif
 #ifndef SPATTN_EOFF
-#define SPATTN_EOFF 2
+#define SPATTN_EOFF 2  // P*V slots before the first probability word of the next block is made
 #endif
 #ifndef SPATTN_EARLY
-#define SPATTN_EARLY 4
+#define SPATTN_EARLY 4  // of the 8 words per query block, those made one step early
 #endif
 #ifndef SPATTN_LEAD512
-#define SPATTN_LEAD512 1
+#define SPATTN_LEAD512 1  // tiles loaded ahead for head size 512
 #endif
 #ifndef SPATTN_BN
-#define SPATTN_BN 64
+#define SPATTN_BN 64  // keys per tile (head sizes 64, 128)
 #endif
 constexpr int pow2_ceil(int x) { return x <= 1 ? 1 : 2 * pow2_ceil((x + 1) / 2); }
 constexpr float kTau = 8.0f;           // lazy-rescale threshold (log2 units)
