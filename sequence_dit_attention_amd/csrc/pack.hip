@@ -74,11 +74,12 @@ __global__ __launch_bounds__(kThreads) void segcopy_kernel(SegArgs a, int64_t o_
 }  // namespace
 
 hipError_t launch_segcopy(const CopySeg* segs, int n, int64_t outer, hipStream_t stream) {
-  for (int base = 0; base < n; base += kMaxSegs) {
+  int i = 0;  // next segment to place; empty ones are skipped, so a batch may span more than kMaxSegs entries
+  while (i < n) {
     SegArgs a{};
     a.nseg = 0;
     int64_t blocks = 0, outer_max = 0;
-    for (int i = base; i < n && a.nseg < kMaxSegs; ++i) {
+    for (; i < n && a.nseg < kMaxSegs; ++i) {
       if (segs[i].nbytes <= 0) continue;
       const int j = a.nseg++;
       a.src[j] = segs[i].src;

@@ -32,6 +32,9 @@ def _host_rand(rng, n, dtype):
     ([40000, 39999], [39999, 0], 80000),
     ([0], [0], 0),
     ([123457], [1], 123460),
+    # 45 ranks, every third one empty: more segments than one copy launch takes (32)
+    ([0 if r % 3 == 1 else 100 + r for r in range(45)],
+     [sum(0 if q % 3 == 1 else 100 + q for q in range(r)) for r in range(45)], 4000),
 ])
 def test_pack_bit_exact(dtype, counts, displs, flat_n):
     rng = np.random.default_rng(sum(counts) + 7)

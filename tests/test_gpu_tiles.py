@@ -15,8 +15,9 @@ from tests._helpers import to_dev, to_host_bits
 
 pytestmark = pytest.mark.gpu
 
+# the last three grids have more blocks than one copy launch takes (32), with empty blocks in between
 GRIDS = [(7, 5, 3, 2, 3), (128, 128, 512, 2, 2), (84, 48, 512, 3, 3), (5, 3, 4, 7, 1), (9, 1, 2, 2, 4),
-         (33, 65, 17, 4, 4), (1, 1, 8, 1, 1)]
+         (33, 65, 17, 4, 4), (1, 1, 8, 1, 1), (3, 2, 8, 3, 20), (2, 50, 3, 5, 10), (40, 40, 6, 6, 7)]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
