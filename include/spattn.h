@@ -271,8 +271,8 @@ int sp_av_positions(int64_t T, int64_t Hh, int64_t Ww, int64_t n_audio, int64_t 
  * gathered).
  * Errors: SP_EINVAL (bad dtype, sq < 0, skv < 1, H < 1, scale not finite or
  * <= 0, null pointers with data), SP_EUNSUPPORTED (other head sizes),
- * SP_ERANGE (sizes beyond the kernel's 32-bit grid, or 64 tokens of K spanning
- * 2 GiB or more), SP_EOVERLAP (o or lse
+ * SP_ERANGE (sq or skv of 2^31 - 256 or more, sizes beyond the kernel's 32-bit
+ * grid, or 64 tokens of K spanning 2 GiB or more), SP_EOVERLAP (o or lse
  * overlaps an input or each other), SP_EHIP.  sq == 0 enqueues nothing.
  */
 int shard_attn_fwd(int32_t dtype, const void* q, const void* k, const void* v,

@@ -97,6 +97,7 @@ int check_attn(const char* fn, int32_t dtype, int64_t sq, int64_t skv, int32_t H
   // Grid: one work-group per (32-query tile, head) at most; keep it inside 2^31.
   if ((sq + 31) / 32 > spattn::kMaxGrid / H) return fail(SP_ERANGE, "%s: sq*H too large for one launch", fn);
   if (skv > (int64_t(1) << 31) - 256) return fail(SP_ERANGE, "%s: skv must be < 2^31", fn);
+  if (sq > (int64_t(1) << 31) - 256) return fail(SP_ERANGE, "%s: sq must be < 2^31", fn);
   // The kernels address a 64-token K/V tile with 32-bit byte offsets.
   if (int64_t(H) * d * 4 * 64 > (int64_t(1) << 31) - 1)
     return fail(SP_ERANGE, "%s: H*d too large (64 tokens of K must span < 2 GiB)", fn);

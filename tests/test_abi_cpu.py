@@ -215,6 +215,8 @@ def test_attn_validation():
     assert f(1, q, k, v, o, o + 8, 10, 20, 2, 128, 0.1, None) == SP_EOVERLAP
     assert f(1, None, k, v, o, None, 10, 20, 2, 128, 0.1, None) == SP_EINVAL
     assert f(1, q, k, v, o, None, 0, 20, 2, 128, 0.1, None) == 0   # sq == 0: nothing enqueued
+    assert f(1, q, k, v, o, None, 2**31, 20, 1, 128, 0.1, None) == SP_ERANGE  # sq beyond 32-bit row indices
+    assert f(1, q, k, v, o, None, 10, 2**31, 1, 128, 0.1, None) == SP_ERANGE  # skv likewise
 
 
 def test_attn_gv_validation():
