@@ -13,6 +13,7 @@ from .spattn_oracle import (  # noqa: F401
     shard_bounds,
     all_shard_bounds,
     allgatherv_layout,
+    allgatherv_layout_lens,
     varlen_pack,
     varlen_unpack,
     rope_inv_freq,

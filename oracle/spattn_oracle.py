@@ -78,6 +78,33 @@ def allgatherv_layout(S: int, W: int, outer: int = 1, inner: int = 1):
     return counts, displs
 
 
+def allgatherv_layout_lens(seq_lens, outer: int = 1, inner: int = 1):
+    """AllGatherV counts and displacements for arbitrary per-rank lengths  [MH3, 后端 A].
+
+    exchange(rank, tensors, cat_dims) gathers tensors that agree outside the
+    concatenation axis; rank r's tensor is viewed as [outer, seq_lens[r], inner]
+    (outer = product of the sizes before cat_dim, inner = product after it).
+    Its block in the flat receive buffer holds every one of its elements:
+    counts[r] = outer * seq_lens[r] * inner, the blocks back to back in rank
+    order: displs[r] = counts[0] + ... + counts[r-1].  Written as element
+    counting loops over Python ints.
+    """
+    outer, inner = int(outer), int(inner)
+    if outer < 0 or inner < 0 or any(int(s) < 0 for s in seq_lens) or len(seq_lens) < 1:
+        raise ValueError("need at least one rank and non-negative sizes")
+    counts, displs = [], []
+    next_free = 0
+    for s in seq_lens:
+        n = 0
+        for _o in range(outer):
+            for _t in range(int(s)):
+                n += inner
+        counts.append(n)
+        displs.append(next_free)
+        next_free += n
+    return counts, displs
+
+
 # ---------------------------------------------------------------------------
 # AllGatherV data movement  [MH3, 后端 A]
 # ---------------------------------------------------------------------------

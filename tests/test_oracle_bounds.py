@@ -74,3 +74,48 @@ def test_layout():
         for r in range(1, W):
             assert displs[r] == displs[r - 1] + counts[r - 1]
         assert sum(counts) == outer * S * inner
+
+
+def test_layout_lens_matches_numpy_concatenation():
+    """counts/displs of arbitrary per-rank lengths are where numpy's own
+    concatenation of the flattened rank tensors puts each rank's elements."""
+    import numpy as np
+
+    for lens, outer, inner in [([3, 0, 5, 1], 2, 4), ([4095, 4096, 4096, 4096], 1, 16 * 128), ([0], 3, 2),
+                               ([2, 7], 1, 1), ([1, 1, 1], 5, 0), ([6, 2, 9], 0, 3)]:
+        counts, displs = oracle.allgatherv_layout_lens(lens, outer, inner)
+        tensors = [np.arange(outer * s * inner, dtype=np.int64).reshape(outer, s, inner) + 10**9 * (r + 1)
+                   for r, s in enumerate(lens)]
+        flat = np.concatenate([t.ravel() for t in tensors]) if tensors else np.zeros(0)
+        assert flat.size == sum(counts)
+        for r, t in enumerate(tensors):
+            assert counts[r] == t.size
+            assert np.array_equal(flat[displs[r]:displs[r] + counts[r]], t.ravel())
+
+
+def test_layout_lens_concat_on_a_middle_axis():
+    """exchange(rank, tensors, cat_dims) on axis 1 of [2, s_r, 3, 4] tensors:
+    pack by the layout, unpack with outer = 2, inner = 12, and the result is
+    numpy's concatenation along that axis."""
+    import numpy as np
+
+    rng = np.random.default_rng(11)
+    lens = [2, 5, 0, 3]
+    tensors = [rng.integers(0, 1000, size=(2, s, 3, 4)) for s in lens]
+    counts, displs = oracle.allgatherv_layout_lens(lens, 2, 12)
+    assert sum(counts) == sum(t.size for t in tensors)
+    flat = oracle.varlen_pack([t.ravel() for t in tensors], counts, displs, np.zeros(sum(counts), np.int64))
+    out = oracle.varlen_unpack(flat, displs, lens, 2, 12).reshape(2, sum(lens), 3, 4)
+    assert np.array_equal(out, np.concatenate(tensors, axis=1))
+
+
+def test_layout_lens_equals_split_layout():
+    for S, W, outer, inner in [(16383, 4, 1, 2048), (7, 4, 3, 5), (3, 8, 2, 1)]:
+        lens = [b - a for a, b in oracle.all_shard_bounds(S, W)]
+        assert oracle.allgatherv_layout_lens(lens, outer, inner) == oracle.allgatherv_layout(S, W, outer, inner)
+
+
+@pytest.mark.parametrize("args", [([], 1, 1), ([1, -1], 1, 1), ([1], -1, 1), ([1], 1, -2)])
+def test_layout_lens_invalid(args):
+    with pytest.raises(ValueError):
+        oracle.allgatherv_layout_lens(*args)

@@ -117,6 +117,16 @@ def _rms_eps_outside(x, gamma, eps):
     return x / (np.sqrt(np.mean(x * x, axis=-1, keepdims=True)) + eps) * gamma
 
 
+def _layout_lens_inclusive(seq_lens, outer=1, inner=1):  # displacement counts the rank's own block
+    counts = [int(outer) * int(n) * int(inner) for n in seq_lens]
+    return counts, [sum(counts[:r + 1]) for r in range(len(counts))]
+
+
+def _layout_lens_no_outer(seq_lens, outer=1, inner=1):  # outer dropped from the counts
+    counts = [int(n) * int(inner) for n in seq_lens]
+    return counts, [sum(counts[:r]) for r in range(len(counts))]
+
+
 def _tiles_transposed(Hh, Ww, pr, pc, p):  # process p read column-major over the block grid
     i, j = p % pr, p // pr
     return (Hh * i) // pr, (Hh * (i + 1)) // pr, (Ww * j) // pc, (Ww * (j + 1)) // pc
@@ -146,6 +156,10 @@ CASES = {
     "attention: softmax over the queries": ({"attention": _attn_softmax_over_queries}, ATTN_PINS),
     "rms_norm: mean subtracted": ({"rms_norm": _layer_norm}, [tq.test_rms_norm_by_loops]),
     "rms_norm: eps outside the root": ({"rms_norm": _rms_eps_outside}, [tq.test_rms_norm_by_loops]),
+    "layout: displacements include the rank's own block": ({"allgatherv_layout_lens": _layout_lens_inclusive},
+                                                           [tb.test_layout_lens_matches_numpy_concatenation]),
+    "layout: outer dropped from the counts": ({"allgatherv_layout_lens": _layout_lens_no_outer},
+                                              [tb.test_layout_lens_concat_on_a_middle_axis]),
     "tiles: block grid read column-major": ({"tile_bounds": _tiles_transposed},
                                             [lambda: tt.test_every_pixel_in_exactly_one_block(7, 5, 2, 3)]),
 }
