@@ -94,6 +94,26 @@ int sp_allgatherv_layout(int64_t S, int32_t W, int64_t outer, int64_t inner,
                          int64_t* counts, int64_t* displs);
 
 /*
+ * sp_allgatherv_layout_lens -- AllGatherV counts and displacements for any
+ * per-rank lengths along any concatenation axis (elements).
+ * Defined by section 后端 A of the same page: exchange(rank, tensors,
+ * cat_dims) gathers tensors that agree outside the concatenation axis, with
+ * counts = element counts per rank and displacements = target offsets in the
+ * flat receive buffer.  Rank r's tensor is viewed as [outer, seq_lens[r],
+ * inner] (outer = product of the sizes before the concatenation axis, inner =
+ * product after it); counts[r] = outer*seq_lens[r]*inner and displs[r] =
+ * counts[0] + ... + counts[r-1] (rank order, no gaps).  With seq_lens from
+ * sp_shard_bounds it equals sp_allgatherv_layout.
+ *   seq_lens  host array of W lengths along the concatenation axis (>= 0)
+ *   counts, displs  host arrays of W entries written by the call (untouched
+ *                   on error)
+ * Errors: SP_EINVAL (W < 1, a negative length, outer or inner, null arrays),
+ * SP_ERANGE (outer*sum(seq_lens)*inner overflows int64).  Host-only.
+ */
+int sp_allgatherv_layout_lens(int32_t W, const int64_t* seq_lens, int64_t outer, int64_t inner,
+                              int64_t* counts, int64_t* displs);
+
+/*
  * varlen_pack -- the data movement of one AllGatherV into a flat buffer.
  * Defined by section 后端 A: for every rank r and 0 <= i < counts[r],
  * flat[displs[r] + i] = send[r][i].  Bits are copied unchanged; elements of

@@ -16,6 +16,7 @@ from .api import (  # noqa: F401
     split_workspace_bytes,
     sp_abi_version,
     sp_allgatherv_layout,
+    sp_allgatherv_layout_lens,
     sp_av_positions,
     sp_shard_bounds,
     sp_tile_bounds,

@@ -14,6 +14,7 @@ SIGNATURES = [
     ("sp_last_error", ctypes.c_char_p, []),
     ("sp_shard_bounds", ctypes.c_int, [_I64, _I32, _I32, _PI64, _PI64]),
     ("sp_allgatherv_layout", ctypes.c_int, [_I64, _I32, _I64, _I64, _PI64, _PI64]),
+    ("sp_allgatherv_layout_lens", ctypes.c_int, [_I32, _PI64, _I64, _I64, _PI64, _PI64]),
     ("varlen_pack", ctypes.c_int, [_I32, _I32, ctypes.POINTER(_VP), _PI64, _PI64, _VP, _I64, _VP]),
     ("varlen_unpack", ctypes.c_int, [_I32, _I32, _VP, _I64, _PI64, _PI64, _I64, _I64, _VP, _VP]),
     ("rope_apply", ctypes.c_int, [_I32, _VP, _VP, _I64, _I32, _I32, _I64, ctypes.c_double, _I32, _VP]),

@@ -60,6 +60,15 @@ def sp_allgatherv_layout(S: int, W: int, outer: int = 1, inner: int = 1):
     return list(counts)[:W], list(displs)[:W]
 
 
+def sp_allgatherv_layout_lens(seq_lens, outer: int = 1, inner: int = 1):
+    """AllGatherV (counts, displs) of tensors [outer, seq_lens[r], inner], blocks in rank order."""
+    W = len(seq_lens)
+    counts, displs = (ctypes.c_int64 * max(W, 1))(), (ctypes.c_int64 * max(W, 1))()
+    check("sp_allgatherv_layout_lens",
+          lib().sp_allgatherv_layout_lens(W, _i64s(seq_lens) if W else None, outer, inner, counts, displs))
+    return list(counts)[:W], list(displs)[:W]
+
+
 def varlen_pack(sends, counts, displs, flat: torch.Tensor) -> torch.Tensor:
     """flat[displs[r] : displs[r] + counts[r]] = sends[r] (flattened), in place on `flat`."""
     code = _dtype_code(flat)
@@ -261,20 +270,34 @@ def shard_attn_fwd_split(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, nspl
 
 def exchange_sim(shards, cat_dim: int = 0):
     """Single-GPU stand-in for exchange(rank, tensors, cat_dims): AllGatherV of
-    per-rank shards (list of tensors equal except along cat_dim) through a flat
-    buffer, then narrow/view/concat.  Returns the concatenated tensor."""
+    per-rank shards (tensors of one dtype and device that agree in every size
+    except along cat_dim) through a flat buffer, then narrow/view/concat.
+    Counts and displacements come from sp_allgatherv_layout_lens.  Returns the
+    concatenated tensor."""
+    shards = list(shards)
+    if not shards:
+        raise ValueError("exchange_sim needs at least one shard")
     ref = shards[0]
+    nd = ref.dim()
+    if nd == 0:
+        raise ValueError("shards must have at least one dimension")
+    if not -nd <= cat_dim < nd:
+        raise ValueError(f"cat_dim {cat_dim} out of range for {nd}-d shards")
+    cat_dim %= nd
     shape = list(ref.shape)
+    for r, s in enumerate(shards):
+        if s.dtype != ref.dtype or s.device != ref.device:
+            raise TypeError(f"shard {r} differs from shard 0 in dtype or device")
+        if s.dim() != nd or any(s.shape[i] != shape[i] for i in range(nd) if i != cat_dim):
+            raise ValueError(f"shard {r} has shape {tuple(s.shape)}: shards may differ only along dim {cat_dim}")
+        if not s.is_contiguous():
+            raise ValueError(f"shard {r} must be contiguous")
     outer = math.prod(shape[:cat_dim])
     inner = math.prod(shape[cat_dim + 1:])
     lens = [int(s.shape[cat_dim]) for s in shards]
-    counts = [outer * n * inner for n in lens]
-    displs, off = [], 0
-    for c in counts:
-        displs.append(off)
-        off += c
-    flat = torch.empty(off, dtype=ref.dtype, device=ref.device)
-    varlen_pack([s.reshape(-1) for s in shards], counts, displs, flat)
+    counts, displs = sp_allgatherv_layout_lens(lens, outer, inner)
+    flat = torch.empty(sum(counts), dtype=ref.dtype, device=ref.device)
+    varlen_pack([s.view(-1) for s in shards], counts, displs, flat)
     shape[cat_dim] = sum(lens)
     out = torch.empty(shape, dtype=ref.dtype, device=ref.device)
     varlen_unpack(flat, displs, lens, outer, inner, out)

@@ -143,6 +143,29 @@ int sp_allgatherv_layout(int64_t S, int32_t W, int64_t outer, int64_t inner, int
   return ok();
 }
 
+int sp_allgatherv_layout_lens(int32_t W, const int64_t* seq_lens, int64_t outer, int64_t inner, int64_t* counts,
+                              int64_t* displs) {
+  const char* fn = "sp_allgatherv_layout_lens";
+  if (!seq_lens || !counts || !displs) return fail(SP_EINVAL, "%s: null host array", fn);
+  if (W < 1) return fail(SP_EINVAL, "%s: W must be >= 1 (got %d)", fn, W);
+  if (outer < 0 || inner < 0) return fail(SP_EINVAL, "%s: outer and inner must be >= 0", fn);
+  // Validate everything before writing an output.
+  int64_t off = 0;
+  for (int32_t r = 0; r < W; ++r) {
+    if (seq_lens[r] < 0) return fail(SP_EINVAL, "%s: seq_lens[%d] < 0", fn, r);
+    int64_t n;
+    if (!mul_ok(outer, seq_lens[r], &n) || !mul_ok(n, inner, &n) || !add_ok(off, n, &off))
+      return fail(SP_ERANGE, "%s: outer*sum(seq_lens)*inner overflows int64", fn);
+  }
+  off = 0;
+  for (int32_t r = 0; r < W; ++r) {
+    counts[r] = outer * seq_lens[r] * inner;  // checked above
+    displs[r] = off;
+    off += counts[r];
+  }
+  return ok();
+}
+
 int varlen_pack(int32_t dtype, int32_t W, const void* const* send, const int64_t* counts,
                 const int64_t* displs, void* flat, int64_t flat_elems, void* stream) {
   const int eb = elem_bytes(dtype);

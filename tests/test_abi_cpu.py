@@ -28,7 +28,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert "shard_attn_fwd" in names and "shard_attn_fwd_gv" in names and len(names) == 17
+    assert "shard_attn_fwd" in names and "shard_attn_fwd_gv" in names and len(names) == 18
     h = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
         assert hasattr(h, n), n
@@ -46,6 +46,44 @@ def test_shard_bounds_match_oracle():
 def test_layout_matches_oracle():
     for S, W, outer, inner in [(16383, 4, 1, 2048), (1001, 4, 1, 128), (7, 4, 3, 5), (3, 8, 2, 1)]:
         assert api.sp_allgatherv_layout(S, W, outer, inner) == oracle.allgatherv_layout(S, W, outer, inner)
+
+
+def test_layout_lens_matches_oracle():
+    for lens, outer, inner in [([4095, 4096, 4096, 4096], 1, 16 * 128), ([3, 0, 5, 1], 2, 4), ([0], 3, 2),
+                               ([2, 7], 1, 1), ([1, 1, 1], 5, 0), ([6, 2, 9], 0, 3), ([250, 250, 250, 251], 1, 128)]:
+        assert api.sp_allgatherv_layout_lens(lens, outer, inner) == oracle.allgatherv_layout_lens(lens, outer, inner)
+    for S, W in [(16383, 4), (367287, 4), (7, 8)]:
+        lens = [b - a for a, b in oracle.all_shard_bounds(S, W)]
+        assert api.sp_allgatherv_layout_lens(lens, 1, 3072) == api.sp_allgatherv_layout(S, W, 1, 3072)
+
+
+def test_layout_lens_errors_leave_outputs_untouched():
+    L = _lib.lib()
+    c, d = (ctypes.c_int64 * 3)(-7, -7, -7), (ctypes.c_int64 * 3)(-7, -7, -7)
+    assert L.sp_allgatherv_layout_lens(3, _arr([1, 2, -1]), 1, 1, c, d) == SP_EINVAL
+    assert L.sp_allgatherv_layout_lens(3, _arr([2**42, 2**42, 2**42]), 2**10, 2**10, c, d) == SP_ERANGE
+    assert b"overflow" in L.sp_last_error()
+    assert L.sp_allgatherv_layout_lens(0, _arr([1]), 1, 1, c, d) == SP_EINVAL
+    assert L.sp_allgatherv_layout_lens(3, None, 1, 1, c, d) == SP_EINVAL
+    assert L.sp_allgatherv_layout_lens(3, _arr([1, 2, 3]), -1, 1, c, d) == SP_EINVAL
+    assert L.sp_allgatherv_layout_lens(3, _arr([1, 2, 3]), 1, 1, None, d) == SP_EINVAL
+    assert list(c) == [-7, -7, -7] and list(d) == [-7, -7, -7]
+
+
+def test_exchange_sim_validates_shards():
+    import torch
+
+    a = torch.zeros(2, 3, 4)
+    with pytest.raises(ValueError, match="at least one"):
+        api.exchange_sim([])
+    with pytest.raises(ValueError, match="out of range"):
+        api.exchange_sim([a], 3)
+    with pytest.raises(ValueError, match="differ only along"):
+        api.exchange_sim([a, torch.zeros(2, 3, 5)], 1)
+    with pytest.raises(ValueError, match="differ only along"):
+        api.exchange_sim([a, torch.zeros(2, 3)], 0)
+    with pytest.raises(TypeError, match="dtype or device"):
+        api.exchange_sim([a, torch.zeros(2, 3, 4, dtype=torch.float64)], -1)
 
 
 def _code(fn, *args):

@@ -94,7 +94,7 @@ def test_uneven_workload_kv_pack():
 
 def test_exchange_sim_cat_dims():
     x = torch.randn(2, 37, 3, 4, device="cuda").to(torch.bfloat16)
-    for cat_dim in (0, 1, 2):
+    for cat_dim in (0, 1, 2, -1, -4):
         n = x.shape[cat_dim]
         cuts = [0, n // 3, n // 3, n]  # includes an empty shard
         shards = [x.narrow(cat_dim, cuts[i], cuts[i + 1] - cuts[i]).contiguous() for i in range(3)]
