@@ -34,6 +34,11 @@
  *  - Every argument is validated on the host before anything is enqueued; on
  *    error nothing is enqueued, a negative status is returned and
  *    sp_last_error() describes the failure.  There is no fallback path.
+ *    This includes the size of every launch a call would make: a HIP grid
+ *    holds at most 2^32 - 1 work-items, and a call needing more returns
+ *    SP_ERANGE.  SP_EHIP (the runtime refusing a launch that passed those
+ *    checks) is the one status after which launches of the same call that
+ *    came before the refused one may still run.
  */
 #ifndef SPATTN_H
 #define SPATTN_H
@@ -289,11 +294,17 @@ int sp_av_positions(int64_t T, int64_t Hh, int64_t Ww, int64_t n_audio, int64_t 
  * all channels of a VAE feature map, page "NPU HunyuanImage-3.0模型推理优化
  * 实践", section VAE并行优化, where K and V of all spatial blocks are
  * gathered).
+ * Alignment: SP_BF16 moves Q, K and V in 16-byte vectors and O in 8-byte
+ * ones, so q, k, v and o must be 16-byte aligned (SP_F32: 4-byte, the
+ * element size); lse must be 4-byte aligned.  A token-row slice of a
+ * torch allocation qualifies, since a bf16 row of H*d elements spans a
+ * multiple of 128 bytes for d = 64, 128 and 512.
  * Errors: SP_EINVAL (bad dtype, sq < 0, skv < 1, H < 1, scale not finite or
- * <= 0, null pointers with data), SP_EUNSUPPORTED (other head sizes),
- * SP_ERANGE (sq or skv of 2^31 - 256 or more, sizes beyond the kernel's 32-bit
- * grid, or 64 tokens of K spanning 2 GiB or more), SP_EOVERLAP (o or lse
- * overlaps an input or each other), SP_EHIP.  sq == 0 enqueues nothing.
+ * <= 0, null pointers with data, a misaligned pointer), SP_EUNSUPPORTED
+ * (other head sizes), SP_ERANGE (sq or skv of 2^31 - 256 or more, a grid
+ * beyond 2^32 - 1 work-items, or 64 tokens of K spanning 2 GiB or more),
+ * SP_EOVERLAP (o or lse overlaps an input or each other), SP_EHIP.
+ * sq == 0 enqueues nothing.
  */
 int shard_attn_fwd(int32_t dtype, const void* q, const void* k, const void* v,
                    void* o, float* lse, int64_t sq, int64_t skv, int32_t H, int32_t d,
@@ -319,7 +330,9 @@ int shard_attn_fwd(int32_t dtype, const void* q, const void* k, const void* v,
  *               on entry do not matter and are overwritten
  * Errors: as shard_attn_fwd, plus SP_EUNSUPPORTED (SP_F32), SP_EINVAL (nsplit
  * out of range, null or misaligned workspace), SP_ERANGE (workspace too
- * small), SP_EOVERLAP (workspace overlaps another buffer).
+ * small; the attention grid over all ranges or the merge grid, one thread per
+ * four output columns, beyond 2^32 - 1 work-items: both are checked before
+ * either launch), SP_EOVERLAP (workspace overlaps another buffer).
  */
 int shard_attn_fwd_split(int32_t dtype, const void* q, const void* k, const void* v, void* o, float* lse,
                          int64_t sq, int64_t skv, int32_t H, int32_t d, float scale, int32_t nsplit,
@@ -349,7 +362,8 @@ int64_t sp_attn_split_workspace(int64_t sq, int32_t H, int32_t d, int32_t nsplit
  *   seq_lens   host array of W token counts (>= 0, sum >= 1)
  *   o, lse, sq, H, d, scale, stream  as in shard_attn_fwd
  * Errors: as shard_attn_fwd, plus SP_EINVAL (W < 1, null host arrays, a
- * negative length, a null shard with tokens), SP_EUNSUPPORTED (W > 16, or
+ * negative length, a null shard with tokens, a shard with tokens not aligned
+ * as k and v must be), SP_EUNSUPPORTED (W > 16, or
  * d = 512: head sizes 64 and 128 only),
  * SP_ERANGE (lengths overflow), SP_EOVERLAP (o or lse overlaps q, a shard or
  * each other).  sq == 0 enqueues nothing.

@@ -863,8 +863,8 @@ template <int D, int DV, bool GV, bool SPLIT = false>
 hipError_t launch_d(const void* q, const KvArg<GV>& kv, void* o, float* lse, int64_t sq, int64_t skv, int H,
                     float c, hipStream_t stream, int nsplit = 1, float* opart = nullptr) {
   const int64_t nqt = (sq + Geo<D, DV>::BM - 1) / Geo<D, DV>::BM;
-  const int64_t grid = nqt * H * (D / DV) * nsplit;
-  if (grid > kMaxGrid) return hipErrorInvalidConfiguration;
+  const int64_t grid = nqt * H * (D / DV) * nsplit;  // the host has checked grid * kThreads <= kMaxItems
+  if (grid > kMaxItems / kThreads) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((attn_bf16_kernel<D, DV, GV, SPLIT>), dim3(unsigned(grid)), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(q), kv, static_cast<uint16_t*>(o), lse, int(sq), int(skv), H, c,
                      int(nqt), nsplit, opart);
@@ -906,18 +906,33 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ op
 template <int D, int DV>
 hipError_t launch_split(const void* q, const void* k, const void* v, void* o, float* lse, int64_t sq, int64_t skv,
                         int H, float c, int nsplit, float* opart, float* lpart, hipStream_t stream) {
+  // Both grids are checked before the first launch, so a call that does not
+  // fit enqueues nothing.
+  if (attn_bf16_items(sq, H, D, nsplit) > kMaxItems || attn_merge_items(sq, H, D) > kMaxItems)
+    return hipErrorInvalidConfiguration;
   const KvFlat kv{static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v)};
   hipError_t e = launch_d<D, DV, false, true>(q, kv, o, lpart, sq, skv, H, c, stream, nsplit, opart);
   if (e != hipSuccess) return e;
   const int64_t threads = sq * H * (D / 4);
-  const int64_t blocks = (threads + 255) / 256;
-  if (blocks > kMaxGrid) return hipErrorInvalidConfiguration;
+  const int64_t blocks = (threads + 255) / 256;  // checked with the attention grid before either launch
   hipLaunchKernelGGL(merge_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, opart, lpart,
                      static_cast<uint16_t*>(o), lse, nsplit, sq, H, D);
   return hipGetLastError();
 }
 
 }  // namespace
+
+int64_t attn_bf16_items(int64_t sq, int H, int d, int nsplit) {
+  const int bm = d == 512 ? Geo<512, 256>::BM : Geo<128>::BM;
+  const int ncb = d == 512 ? 2 : 1;
+  const __int128 n = __int128((sq + bm - 1) / bm) * H * ncb * nsplit * kThreads;
+  return n > INT64_MAX ? INT64_MAX : int64_t(n);
+}
+
+int64_t attn_merge_items(int64_t sq, int H, int d) {
+  const __int128 n = (__int128(sq) * H * (d / 4) + 255) / 256 * 256;
+  return n > INT64_MAX ? INT64_MAX : int64_t(n);
+}
 
 hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int64_t sq,
                             int64_t skv, int H, int d, float scale, hipStream_t stream) {

@@ -107,8 +107,8 @@ template <bool GV>
 hipError_t launch_any(const float* q, const KvArgF32<GV>& kv, float* o, float* lse, int64_t sq, int64_t skv,
                       int H, int d, float scale, hipStream_t stream) {
   const int64_t nqt = (sq + kRows - 1) / kRows;
-  const int64_t grid = nqt * H;
-  if (grid > kMaxGrid) return hipErrorInvalidConfiguration;
+  const int64_t grid = nqt * H;  // the host has checked grid * kRows <= kMaxItems
+  if (grid > kMaxItems / kRows) return hipErrorInvalidConfiguration;
   const float c = scale * 1.4426950408889634f;
   if (d == 64)
     hipLaunchKernelGGL((attn_f32_kernel<64, GV>), dim3(unsigned(grid)), dim3(kRows), 0, stream, q, kv, o, lse, sq,
@@ -120,6 +120,11 @@ hipError_t launch_any(const float* q, const KvArgF32<GV>& kv, float* o, float* l
 }
 
 }  // namespace
+
+int64_t attn_f32_items(int64_t sq, int H) {
+  const __int128 n = __int128((sq + kRows - 1) / kRows) * H * kRows;
+  return n > INT64_MAX ? INT64_MAX : int64_t(n);
+}
 
 hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                            int64_t sq, int64_t skv, int H, int d, float scale, hipStream_t stream) {

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 #include <vector>
 
 #include "../../include/spattn.h"
@@ -65,8 +66,18 @@ bool blocks_disjoint(int32_t W, const int64_t* displs, const std::vector<int64_t
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+// Launch grids are 32-bit counts of work-items: a call whose launch would
+// exceed that is refused before anything is enqueued.
+int grid_check(const char* fn, int64_t items) {
+  if (items > spattn::kMaxItems)
+    return fail(SP_ERANGE, "%s: a launch would need %lld work-items, more than the 2^32-1 a HIP grid holds", fn,
+                static_cast<long long>(items));
+  return SP_OK;
+}
+
 int launch_copies(const std::vector<CopySeg>& segs, int64_t outer, void* stream) {
   if (segs.empty()) return ok();
+  if (int rc = grid_check("copy", spattn::segcopy_max_items(segs.data(), static_cast<int>(segs.size())))) return rc;
   (void)hipGetLastError();  // launches below report their own status
   hipError_t e = spattn::launch_segcopy(segs.data(), static_cast<int>(segs.size()), outer,
                                         as_stream(stream));
@@ -94,13 +105,24 @@ int check_attn(const char* fn, int32_t dtype, int64_t sq, int64_t skv, int32_t H
   if (!mul_ok(sq, int64_t(H) * d, &qn) || !mul_ok(skv, int64_t(H) * d, &kn) || !mul_ok(qn, eb, qb) ||
       !mul_ok(kn, eb, kb) || !mul_ok(sq, int64_t(H) * 4, lb))
     return fail(SP_ERANGE, "%s: size overflows int64", fn);
-  // Grid: one work-group per (32-query tile, head) at most; keep it inside 2^31.
-  if ((sq + 31) / 32 > spattn::kMaxGrid / H) return fail(SP_ERANGE, "%s: sq*H too large for one launch", fn);
+  if (int rc = grid_check(fn, dtype == SP_BF16 ? spattn::attn_bf16_items(sq, H, d, 1) : spattn::attn_f32_items(sq, H)))
+    return rc;
   if (skv > (int64_t(1) << 31) - 256) return fail(SP_ERANGE, "%s: skv must be < 2^31", fn);
   if (sq > (int64_t(1) << 31) - 256) return fail(SP_ERANGE, "%s: sq must be < 2^31", fn);
   // The kernels address a 64-token K/V tile with 32-bit byte offsets.
   if (int64_t(H) * d * 4 * 64 > (int64_t(1) << 31) - 1)
     return fail(SP_ERANGE, "%s: H*d too large (64 tokens of K must span < 2 GiB)", fn);
+  return SP_OK;
+}
+
+// The bf16 kernels move Q, K and V in 16-byte vectors and O in 8-byte ones;
+// the float32 kernel uses element accesses.  lse is float32.
+int check_attn_align(const char* fn, int32_t dtype, std::initializer_list<const void*> tensors, const float* lse) {
+  const uintptr_t need = dtype == SP_BF16 ? 16 : 4;
+  for (const void* p : tensors)
+    if (reinterpret_cast<uintptr_t>(p) % need)
+      return fail(SP_EINVAL, "%s: q, k, v, o (and every shard) must be %d-byte aligned for this dtype", fn, int(need));
+  if (reinterpret_cast<uintptr_t>(lse) % 4) return fail(SP_EINVAL, "%s: lse must be 4-byte aligned", fn);
   return SP_OK;
 }
 
@@ -265,6 +287,7 @@ int rope_apply(int32_t dtype, const void* x, void* y, int64_t s, int32_t H, int3
   if (!x || !y) return fail(SP_EINVAL, "rope_apply: null device pointer");
   if (x != y && ranges_overlap(x, bytes, y, bytes))
     return fail(SP_EOVERLAP, "rope_apply: x and y overlap without being equal");
+  if (int rc = grid_check("rope_apply", spattn::rope_items(eb, s, d, style, x, y, false))) return rc;
   (void)hipGetLastError();
   hipError_t e = spattn::launch_rope(dtype, x, y, s, H, d, pos0, theta, style, as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "rope launch");
@@ -291,6 +314,7 @@ int rope_apply_mx(int32_t dtype, const void* x, void* y, int64_t s, int32_t H, i
   if (x != y && ranges_overlap(x, bytes, y, bytes)) return fail(SP_EOVERLAP, "%s: x and y overlap without being equal", fn);
   if (ranges_overlap(pos, pbytes, y, bytes)) return fail(SP_EOVERLAP, "%s: positions overlap y", fn);
   const int sec[3] = {sections[0], sections[1], sections[2]};
+  if (int rc = grid_check(fn, spattn::rope_items(eb, s, d, style, x, y, false))) return rc;
   (void)hipGetLastError();
   hipError_t e = spattn::launch_rope_mx(dtype, x, y, s, H, d, pos, sec, theta, style, as_stream(stream));
   if (e != hipSuccess) return hip_fail(e, "rope launch");
@@ -402,6 +426,7 @@ int qk_norm_rope(int32_t dtype, const void* x, void* y, int64_t s, int32_t H, in
                 "%s: d = %d with these buffers: a head row must split into at most 64 lanes of 1, 2, 4 or 8 pairs "
                 "with x and y aligned to that many elements", fn, d);
   const int sec[3] = {pos ? sections[0] : d / 2, pos ? sections[1] : 0, pos ? sections[2] : 0};
+  if (int rc = grid_check(fn, spattn::rope_items(eb, s, d, style, x, y, true))) return rc;
   (void)hipGetLastError();
   hipError_t e = spattn::launch_qk_norm_rope(dtype, x, y, s, H, d, gamma, static_cast<float>(eps), pos0, pos, sec,
                                              theta, style, as_stream(stream));
@@ -441,6 +466,7 @@ int shard_attn_fwd(int32_t dtype, const void* q, const void* k, const void* v, v
   if (int rc = check_attn("shard_attn_fwd", dtype, sq, skv, H, d, scale, true, &qb, &kb, &lb)) return rc;
   if (sq == 0) return ok();
   if (!q || !k || !v || !o) return fail(SP_EINVAL, "shard_attn_fwd: null device pointer");
+  if (int rc = check_attn_align("shard_attn_fwd", dtype, {q, k, v, o}, lse)) return rc;
   if (ranges_overlap(o, qb, q, qb) || ranges_overlap(o, qb, k, kb) || ranges_overlap(o, qb, v, kb))
     return fail(SP_EOVERLAP, "shard_attn_fwd: o overlaps an input");
   if (lse && (ranges_overlap(lse, lb, q, qb) || ranges_overlap(lse, lb, k, kb) ||
@@ -481,6 +507,9 @@ int shard_attn_fwd_split(int32_t dtype, const void* q, const void* k, const void
   if (need < 0) return static_cast<int>(need);
   if (sq == 0) return ok();
   if (!q || !k || !v || !o || !workspace) return fail(SP_EINVAL, "%s: null device pointer", fn);
+  if (int rc = check_attn_align(fn, dtype, {q, k, v, o}, lse)) return rc;
+  if (int rc = grid_check(fn, spattn::attn_bf16_items(sq, H, d, nsplit))) return rc;
+  if (int rc = grid_check(fn, spattn::attn_merge_items(sq, H, d))) return rc;
   if (workspace_bytes < need)
     return fail(SP_ERANGE, "%s: workspace holds %lld bytes, %lld needed", fn, (long long)workspace_bytes,
                 (long long)need);
@@ -525,6 +554,10 @@ int shard_attn_fwd_gv(int32_t dtype, const void* q, int32_t W, const void* const
   if (int rc = check_attn(fn, dtype, sq, skv, H, d, scale, false, &qb, &kb, &lb)) return rc;
   if (sq == 0) return ok();
   if (!q || !o) return fail(SP_EINVAL, "%s: null device pointer", fn);
+  if (int rc = check_attn_align(fn, dtype, {q, o}, lse)) return rc;
+  for (int32_t r = 0; r < W; ++r)
+    if (seq_lens[r] > 0)
+      if (int rc = check_attn_align(fn, dtype, {kv.k[r], kv.v[r]}, nullptr)) return rc;
   const int64_t tok_bytes = int64_t(H) * d * elem_bytes(dtype);
   if (ranges_overlap(o, qb, q, qb)) return fail(SP_EOVERLAP, "%s: o overlaps q", fn);
   if (lse && (ranges_overlap(lse, lb, q, qb) || ranges_overlap(lse, lb, o, qb)))

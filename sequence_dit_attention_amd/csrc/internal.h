@@ -70,7 +70,17 @@ hipError_t launch_attn_bf16_gv(const void* q, const KvShards& kv, void* o, float
 hipError_t launch_attn_f32_gv(const float* q, const KvShards& kv, float* o, float* lse, int64_t sq, int H, int d,
                               float scale, hipStream_t stream);
 
-// Largest grid (work-groups) the attention launchers accept.
-constexpr int64_t kMaxGrid = (int64_t(1) << 31) - 1;
+// A HIP launch's grid size is a 32-bit count of work-items per dimension.
+// The host checks every launch of a call against it before enqueuing any.
+constexpr int64_t kMaxItems = (int64_t(1) << 32) - 1;
+
+// Work-items (grid dimension x) of each launch a call makes, for that check;
+// saturate at INT64_MAX instead of overflowing.
+int64_t attn_bf16_items(int64_t sq, int H, int d, int nsplit);  // the attention kernel
+int64_t attn_merge_items(int64_t sq, int H, int d);              // merge of a split launch
+int64_t attn_f32_items(int64_t sq, int H);
+int64_t rope_items(int eb, int64_t s, int d, int style, const void* x, const void* y, bool norm);
+// Largest work-item count of any one batch launch_segcopy would make.
+int64_t segcopy_max_items(const CopySeg* segs, int n);
 
 }  // namespace spattn

@@ -40,7 +40,8 @@ __global__ __launch_bounds__(kThreads) void segcopy_kernel(SegArgs a, int64_t o_
   const int64_t o = o_base + blockIdx.y;
   if (o >= a.outer[s]) return;  // a segment with fewer outer steps than the launch
   const int64_t off = (blk - a.first_blk[s]) * kChunk;
-  const int64_t n = min(kChunk, a.nbytes[s] - off);
+  const int64_t left = a.nbytes[s] - off;  // int64 throughout: a segment may exceed 2^31 bytes
+  const int64_t n = left < kChunk ? left : kChunk;
   const char* src = a.src[s] + o * a.src_stride[s] + off;
   char* dst = a.dst[s] + o * a.dst_stride[s] + off;
   const int tid = threadIdx.x;
@@ -73,31 +74,59 @@ __global__ __launch_bounds__(kThreads) void segcopy_kernel(SegArgs a, int64_t o_
 
 }  // namespace
 
+namespace {
+
+// Fills one launch's batch with the non-empty segments from segs[i] on (at
+// most kMaxSegs of them); returns the index of the first segment left over.
+int next_batch(const CopySeg* segs, int n, int i, int64_t outer, SegArgs& a, int64_t& blocks, int64_t& outer_max) {
+  a = SegArgs{};
+  a.nseg = 0;
+  blocks = 0;
+  outer_max = 0;
+  for (; i < n && a.nseg < kMaxSegs; ++i) {
+    if (segs[i].nbytes <= 0) continue;
+    const int j = a.nseg++;
+    a.src[j] = segs[i].src;
+    a.dst[j] = segs[i].dst;
+    a.nbytes[j] = segs[i].nbytes;
+    a.src_stride[j] = segs[i].src_stride;
+    a.dst_stride[j] = segs[i].dst_stride;
+    a.outer[j] = segs[i].outer >= 0 ? segs[i].outer : outer;
+    if (a.outer[j] > outer_max) outer_max = a.outer[j];
+    a.first_blk[j] = blocks;
+    blocks += (segs[i].nbytes + kChunk - 1) / kChunk;
+  }
+  a.first_blk[a.nseg] = blocks;
+  return i;
+}
+
+}  // namespace
+
+int64_t segcopy_max_items(const CopySeg* segs, int n) {
+  int64_t most = 0;
+  for (int i = 0; i < n;) {
+    SegArgs a;
+    int64_t blocks, outer_max;
+    i = next_batch(segs, n, i, 0, a, blocks, outer_max);
+    const int64_t items = blocks * int64_t(kThreads);  // blocks <= total bytes / 4 KiB + 32: no overflow
+    if (items > most) most = items;
+  }
+  return most;
+}
+
 hipError_t launch_segcopy(const CopySeg* segs, int n, int64_t outer, hipStream_t stream) {
   int i = 0;  // next segment to place; empty ones are skipped, so a batch may span more than kMaxSegs entries
   while (i < n) {
-    SegArgs a{};
-    a.nseg = 0;
-    int64_t blocks = 0, outer_max = 0;
-    for (; i < n && a.nseg < kMaxSegs; ++i) {
-      if (segs[i].nbytes <= 0) continue;
-      const int j = a.nseg++;
-      a.src[j] = segs[i].src;
-      a.dst[j] = segs[i].dst;
-      a.nbytes[j] = segs[i].nbytes;
-      a.src_stride[j] = segs[i].src_stride;
-      a.dst_stride[j] = segs[i].dst_stride;
-      a.outer[j] = segs[i].outer >= 0 ? segs[i].outer : outer;
-      outer_max = max(outer_max, a.outer[j]);
-      a.first_blk[j] = blocks;
-      blocks += (segs[i].nbytes + kChunk - 1) / kChunk;
-    }
-    a.first_blk[a.nseg] = blocks;
+    SegArgs a;
+    int64_t blocks, outer_max;
+    i = next_batch(segs, n, i, outer, a, blocks, outer_max);
     if (a.nseg == 0) continue;
-    // Grid x covers one outer slice; a segment beyond 2^31 chunks is not reachable
-    // (2^31 * 4 KiB = 8 TiB), so blocks always fits.
+    // Grid x covers one outer slice (the host has checked blocks * kThreads
+    // against the 32-bit grid limit); grid y walks the outer slices in
+    // launches of at most 65,535.
     for (int64_t o = 0; o < outer_max; o += kMaxGridY) {
-      const unsigned gy = static_cast<unsigned>(min(kMaxGridY, outer_max - o));
+      const int64_t rest = outer_max - o;
+      const unsigned gy = static_cast<unsigned>(rest < kMaxGridY ? rest : kMaxGridY);
       hipLaunchKernelGGL(segcopy_kernel, dim3(static_cast<unsigned>(blocks), gy), dim3(kThreads), 0,
                          stream, a, o);
       hipError_t e = hipGetLastError();

@@ -322,7 +322,7 @@ hipError_t launch_rows(const void* x, void* y, int64_t s, int H, int d, const fl
   int lg = 0;
   while ((1 << lg) < groups) ++lg;
   const int64_t blocks = (s + kThreads / 64 - 1) / (kThreads / 64);  // one wave per token
-  if (blocks > kMaxGrid) return hipErrorInvalidConfiguration;
+  if (blocks > kMaxItems / kThreads) return hipErrorInvalidConfiguration;  // checked by the host already
   hipLaunchKernelGGL((rope_rows_kernel<T, PG, IL, NORM>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
                      stream, static_cast<const T*>(x), static_cast<T*>(y), s, H, d, lg, gamma, eps, pos0, pos, n0,
                      n1, l2t);
@@ -346,7 +346,7 @@ hipError_t launch_general(const void* x, void* y, int64_t s, int H, int d, int64
                           int n1, double l2t, hipStream_t stream) {
   const int64_t threads = s * ((d / 2) / PG);
   const int64_t blocks = (threads + kThreads - 1) / kThreads;
-  if (blocks > kMaxGrid) return hipErrorInvalidConfiguration;
+  if (blocks > kMaxItems / kThreads) return hipErrorInvalidConfiguration;  // checked by the host already
   hipLaunchKernelGGL((rope_kernel<T, PG, IL>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream,
                      static_cast<const T*>(x), static_cast<T*>(y), s, H, d, pos0, pos, n0, n1, l2t);
   return hipGetLastError();
@@ -380,6 +380,18 @@ int rows_pairs_per_lane(int d, int style, int eb, const void* x, const void* y) 
     if (addr % vec == 0) return pg;
   }
   return 0;
+}
+
+int64_t rope_items(int eb, int64_t s, int d, int style, const void* x, const void* y, bool norm) {
+  const int pg = rows_pairs_per_lane(d, style, eb, x, y);
+  __int128 n;
+  if (pg || norm) {
+    n = __int128((s + kThreads / 64 - 1) / (kThreads / 64)) * kThreads;  // one wave per token
+  } else {
+    const int per = (d / 2) / (((d / 2) % 4) == 0 ? 4 : 1);  // threads per token of the element-wise kernel
+    n = (__int128(s) * per + kThreads - 1) / kThreads * kThreads;
+  }
+  return n > INT64_MAX ? INT64_MAX : int64_t(n);
 }
 
 hipError_t launch_rope(int dtype, const void* x, void* y, int64_t s, int H, int d, int64_t pos0,

@@ -285,3 +285,57 @@ def test_python_wrapper_raises():
     with pytest.raises(_lib.SpattnError) as ei:
         api.sp_shard_bounds(5, 2, 2)
     assert ei.value.code == SP_EINVAL
+
+
+def test_attn_pointer_alignment():
+    """bf16 attention moves Q/K/V in 16-byte vectors and O in 8-byte ones: every
+    tensor must be 16-byte aligned (float32: 4), lse 4-byte aligned."""
+    L = _lib.lib()
+    f = L.shard_attn_fwd
+    q, k, v, o = FAKE, FAKE * 2, FAKE * 3, FAKE * 4
+    for bad in [(q + 8, k, v, o), (q, k + 2, v, o), (q, k, v + 4, o), (q, k, v, o + 8)]:
+        assert f(1, *bad, None, 10, 20, 2, 128, 0.1, None) == SP_EINVAL
+        assert b"aligned" in L.sp_last_error()
+    assert f(1, q, k, v, o, FAKE * 5 + 2, 10, 20, 2, 128, 0.1, None) == SP_EINVAL   # lse
+    assert f(0, q + 2, k, v, o, None, 10, 20, 2, 64, 0.1, None) == SP_EINVAL        # f32: element alignment
+    P = ctypes.c_void_p
+    g = L.shard_attn_fwd_gv
+    ks, vs = (P * 2)(FAKE * 2, FAKE * 2 + 10_008), (P * 2)(FAKE * 3, FAKE * 3 + 10_000)
+    assert g(1, q, 2, ks, vs, _arr([5, 6]), o, None, 10, 2, 128, 0.1, None) == SP_EINVAL   # K shard 1
+    ks = (P * 2)(FAKE * 2, FAKE * 2 + 10_000)
+    assert g(1, q, 2, ks, vs, _arr([5, 6]), o + 8, None, 10, 2, 128, 0.1, None) == SP_EINVAL
+    # an empty shard's pointer is never read: its alignment does not matter
+    assert g(1, q, 2, (P * 2)(FAKE * 2 + 1, FAKE * 2), (P * 2)(FAKE * 3 + 1, FAKE * 3), _arr([0, 6]), o, None,
+             0, 2, 128, 0.1, None) == 0
+    s = L.shard_attn_fwd_split
+    need = L.sp_attn_split_workspace(64, 1, 512, 2)
+    assert s(1, q, k + 8, v, o, None, 64, 300, 1, 512, 0.04, 2, FAKE * 8, need, None) == SP_EINVAL
+
+
+def test_launch_grids_checked_before_enqueue():
+    """A launch grid holds at most 2^32-1 work-items: calls needing more are
+    refused with SP_ERANGE by the host, before anything is enqueued."""
+    L = _lib.lib()
+    f = L.shard_attn_fwd
+    q, k, v, o = FAKE, FAKE * 2, FAKE * 3, FAKE * 4
+    # 2^23 query tiles x 8 heads x 256 threads = 2^34 work-items
+    assert f(1, q, FAKE * 64, FAKE * 96, FAKE * 128, None, 2**31 - 512, 20, 8, 128, 0.1, None) == SP_ERANGE
+    assert b"work-items" in L.sp_last_error()
+    s = L.shard_attn_fwd_split
+    # split: the plain grid fits (2^26 items) but 1,024 key ranges do not
+    need = L.sp_attn_split_workspace(2**20, 64, 128, 1024)
+    assert need > 0
+    assert s(1, FAKE, FAKE * 2, FAKE * 3, FAKE * 4, None, 2**20, 2**20, 64, 128, 0.08, 1024, FAKE * 64, need,
+             None) == SP_ERANGE
+    assert b"work-items" in L.sp_last_error()
+    # split: the attention fits, its merge (one thread per 4 output columns) does not
+    need = L.sp_attn_split_workspace(2**25, 16, 128, 1)
+    assert s(1, FAKE, FAKE * 2, FAKE * 3, FAKE * 4, None, 2**25, 64, 16, 128, 0.08, 1, FAKE * 64, need,
+             None) == SP_ERANGE
+    assert b"work-items" in L.sp_last_error()
+    # a single 128 GiB copy segment: 2^25 chunks of 4 KiB x 256 threads
+    ptrs = (ctypes.c_void_p * 1)(FAKE)
+    assert L.varlen_pack(1, 1, ptrs, _arr([2**36]), _arr([0]), FAKE * 4, 2**36, None) == SP_ERANGE
+    assert b"work-items" in L.sp_last_error()
+    # RoPE: one wave per token
+    assert L.rope_apply(1, FAKE, FAKE, 2**27, 1, 8, 0, 1e4, 0, None) == SP_ERANGE
