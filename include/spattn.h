@@ -347,6 +347,27 @@ int shard_attn_fwd_split(int32_t dtype, const void* q, const void* k, const void
 int64_t sp_attn_split_workspace(int64_t sq, int32_t H, int32_t d, int32_t nsplit);
 
 /*
+ * shard_attn_fwd_split_noalloc -- shard_attn_fwd_split without a workspace
+ * argument and without any allocation, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The float32 partials live in a 64 MiB device array
+ * inside the library (one per device, held until the process ends), so
+ * sp_attn_split_workspace(sq, H, d, nsplit) must not exceed 67,108,864 bytes
+ * (the 128 x 128 VAE block of 4,096 queries at d = 512 with 4 key ranges needs
+ * 32 MiB).  The array's previous contents are never read.  Every call on one
+ * device shares that device's array: calls that overlap in time on one device
+ * (other streams, other threads) race and must be serialised by the caller.
+ * The device address is looked up on the first call on each device (with it
+ * current); no allocating routine is called.
+ *   arguments as shard_attn_fwd_split, without workspace / workspace_bytes
+ * Errors: as shard_attn_fwd_split, plus SP_ERANGE (partials beyond 64 MiB),
+ * SP_EHIP (the scratch address could not be obtained).
+ */
+int shard_attn_fwd_split_noalloc(int32_t dtype, const void* q, const void* k, const void* v, void* o,
+                                 float* lse, int64_t sq, int64_t skv, int32_t H, int32_t d, float scale,
+                                 int32_t nsplit, void* stream);
+
+/*
  * shard_attn_fwd_gv -- shard_attn_fwd against K/V left in the W per-rank
  * shards, without the gather into one buffer.  Section 后端 A reassembles
  * the full sequence by concatenating the ranks' blocks in rank order; here

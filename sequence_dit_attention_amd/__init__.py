@@ -13,6 +13,7 @@ from .api import (  # noqa: F401
     shard_attn_fwd,
     shard_attn_fwd_gv,
     shard_attn_fwd_split,
+    shard_attn_fwd_split_noalloc,
     split_workspace_bytes,
     sp_abi_version,
     sp_allgatherv_layout,

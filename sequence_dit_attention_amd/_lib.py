@@ -27,6 +27,8 @@ SIGNATURES = [
     ("tile_unpack", ctypes.c_int, [_I32, _VP, _I64, _I64, _I64, _I64, _I32, _I32, _VP, _VP]),
     ("shard_attn_fwd_split", ctypes.c_int, [_I32, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I32, _I32, ctypes.c_float,
                                             _I32, _VP, _I64, _VP]),
+    ("shard_attn_fwd_split_noalloc", ctypes.c_int, [_I32, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I32, _I32,
+                                                    ctypes.c_float, _I32, _VP]),
     ("sp_attn_split_workspace", ctypes.c_int64, [_I64, _I32, _I32, _I32]),
     ("sp_av_positions", ctypes.c_int, [_I64, _I64, _I64, _I64, _I64, _I64, _PI64]),
     ("shard_attn_fwd", ctypes.c_int, [_I32, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I32, _I32,

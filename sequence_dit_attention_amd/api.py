@@ -268,6 +268,33 @@ def shard_attn_fwd_split(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, nspl
     return out
 
 
+def shard_attn_fwd_split_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, nsplit: int,
+                                 out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                                 scale: float | None = None) -> torch.Tensor:
+    """shard_attn_fwd_split with its float32 partials in the library's device scratch (no workspace, no
+    allocation inside the call; calls that overlap on one device race)."""
+    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape or q.shape[1:] != k.shape[1:]:
+        raise ValueError("q [sq,H,d], k and v [skv,H,d] with matching H, d")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v dtypes differ")
+    sq, H, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    lp = None
+    if lse is not None:
+        if lse.dtype != torch.float32 or lse.shape != (H, sq):
+            raise ValueError("lse must be float32 [H, sq]")
+        lp = _dev(lse, "lse")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    check("shard_attn_fwd_split_noalloc", lib().shard_attn_fwd_split_noalloc(
+        _dtype_code(q), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(out, "out"), lp, sq, k.shape[0], H, d,
+        float(scale), int(nsplit), _stream(q)))
+    return out
+
+
 def exchange_sim(shards, cat_dim: int = 0):
     """Single-GPU stand-in for exchange(rank, tensors, cat_dims): AllGatherV of
     per-rank shards (tensors of one dtype and device that agree in every size

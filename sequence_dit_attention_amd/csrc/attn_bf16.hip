@@ -52,6 +52,7 @@
 // of the row's position inside a tile.
 #include "internal.h"
 
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -951,6 +952,37 @@ hipError_t launch_attn_bf16_gv(const void* q, const KvShards& kv, void* o, float
   const int64_t skv = kv.start[kv.W];
   if (d == 64) return launch_d<64, 64, true>(q, kv, o, lse, sq, skv, H, c, stream);
   return launch_d<128, 128, true>(q, kv, o, lse, sq, skv, H, c, stream);
+}
+
+namespace {
+
+// Partials of shard_attn_fwd_split_noalloc.  Its contents are never read
+// before being written: every partial row and LSE the merge reads is written
+// by the attention kernel of the same call first, so nothing is cleared.
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+}  // namespace
+
+hipError_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    // The array's host-side name is only a handle: the device address of this
+    // device's copy comes from the runtime, with the device current.
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_attn_bf16_split(const void* q, const void* k, const void* v, void* o, float* lse, int64_t sq,

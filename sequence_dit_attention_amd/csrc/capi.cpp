@@ -494,43 +494,89 @@ int64_t sp_attn_split_workspace(int64_t sq, int32_t H, int32_t d, int32_t nsplit
   return ((ob + 255) / 256) * 256 + lbytes;
 }
 
-int shard_attn_fwd_split(int32_t dtype, const void* q, const void* k, const void* v, void* o, float* lse,
-                         int64_t sq, int64_t skv, int32_t H, int32_t d, float scale, int32_t nsplit,
-                         void* workspace, int64_t workspace_bytes, void* stream) {
-  const char* fn = "shard_attn_fwd_split";
-  int64_t qb, kb, lb;
-  if (int rc = check_attn(fn, dtype, sq, skv, H, d, scale, true, &qb, &kb, &lb)) return rc;
+namespace {
+
+// Validation shared by the split entry points, everything but the
+// workspace: fills the byte sizes of q/o, K (or V) and lse and the workspace
+// the call needs.  *skip is set when sq == 0 (nothing to enqueue).
+int check_split(const char* fn, int32_t dtype, const void* q, const void* k, const void* v, void* o, float* lse,
+                int64_t sq, int64_t skv, int32_t H, int32_t d, float scale, int32_t nsplit, int64_t* qb,
+                int64_t* kb, int64_t* lb, int64_t* need, bool* skip) {
+  *skip = false;
+  if (int rc = check_attn(fn, dtype, sq, skv, H, d, scale, true, qb, kb, lb)) return rc;
   if (dtype != SP_BF16) return fail(SP_EUNSUPPORTED, "%s: bf16 only", fn);
   if (nsplit < 1 || nsplit > 1024 || nsplit > (skv + 63) / 64)
     return fail(SP_EINVAL, "%s: nsplit must be in [1, min(1024, ceil(skv / 64))] (got %d)", fn, nsplit);
-  const int64_t need = sp_attn_split_workspace(sq, H, d, nsplit);
-  if (need < 0) return static_cast<int>(need);
-  if (sq == 0) return ok();
-  if (!q || !k || !v || !o || !workspace) return fail(SP_EINVAL, "%s: null device pointer", fn);
+  *need = sp_attn_split_workspace(sq, H, d, nsplit);
+  if (*need < 0) return static_cast<int>(*need);
+  if (sq == 0) {
+    *skip = true;
+    return SP_OK;
+  }
+  if (!q || !k || !v || !o) return fail(SP_EINVAL, "%s: null device pointer", fn);
   if (int rc = check_attn_align(fn, dtype, {q, k, v, o}, lse)) return rc;
   if (int rc = grid_check(fn, spattn::attn_bf16_items(sq, H, d, nsplit))) return rc;
   if (int rc = grid_check(fn, spattn::attn_merge_items(sq, H, d))) return rc;
-  if (workspace_bytes < need)
-    return fail(SP_ERANGE, "%s: workspace holds %lld bytes, %lld needed", fn, (long long)workspace_bytes,
-                (long long)need);
-  if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(SP_EINVAL, "%s: workspace must be 256-byte aligned", fn);
-  if (ranges_overlap(o, qb, q, qb) || ranges_overlap(o, qb, k, kb) || ranges_overlap(o, qb, v, kb))
+  if (ranges_overlap(o, *qb, q, *qb) || ranges_overlap(o, *qb, k, *kb) || ranges_overlap(o, *qb, v, *kb))
     return fail(SP_EOVERLAP, "%s: o overlaps an input", fn);
-  if (lse && (ranges_overlap(lse, lb, q, qb) || ranges_overlap(lse, lb, k, kb) ||
-              ranges_overlap(lse, lb, v, kb) || ranges_overlap(lse, lb, o, qb)))
+  if (lse && (ranges_overlap(lse, *lb, q, *qb) || ranges_overlap(lse, *lb, k, *kb) ||
+              ranges_overlap(lse, *lb, v, *kb) || ranges_overlap(lse, *lb, o, *qb)))
     return fail(SP_EOVERLAP, "%s: lse overlaps another buffer", fn);
-  if (ranges_overlap(workspace, need, q, qb) || ranges_overlap(workspace, need, k, kb) ||
-      ranges_overlap(workspace, need, v, kb) || ranges_overlap(workspace, need, o, qb) ||
-      (lse && ranges_overlap(workspace, need, lse, lb)))
-    return fail(SP_EOVERLAP, "%s: workspace overlaps another buffer", fn);
+  return SP_OK;
+}
+
+// Partial outputs at the start of the workspace, partial LSEs after them
+// (at the next 256-byte boundary).
+int launch_split_in(const char* fn, const void* q, const void* k, const void* v, void* o, float* lse, int64_t sq,
+                    int64_t skv, int32_t H, int32_t d, float scale, int32_t nsplit, void* workspace, void* stream) {
   const int64_t ob = sq * H * d * int64_t(nsplit) * 4;
   float* opart = static_cast<float*>(workspace);
   float* lpart = reinterpret_cast<float*>(static_cast<char*>(workspace) + ((ob + 255) / 256) * 256);
   (void)hipGetLastError();
   hipError_t e = spattn::launch_attn_bf16_split(q, k, v, o, lse, sq, skv, H, d, scale, nsplit, opart, lpart,
                                                 as_stream(stream));
-  if (e != hipSuccess) return hip_fail(e, "split attention launch");
+  if (e != hipSuccess) return hip_fail(e, fn);
   return ok();
+}
+
+}  // namespace
+
+int shard_attn_fwd_split(int32_t dtype, const void* q, const void* k, const void* v, void* o, float* lse,
+                         int64_t sq, int64_t skv, int32_t H, int32_t d, float scale, int32_t nsplit,
+                         void* workspace, int64_t workspace_bytes, void* stream) {
+  const char* fn = "shard_attn_fwd_split";
+  int64_t qb, kb, lb, need;
+  bool skip;
+  if (int rc = check_split(fn, dtype, q, k, v, o, lse, sq, skv, H, d, scale, nsplit, &qb, &kb, &lb, &need, &skip))
+    return rc;
+  if (skip) return ok();
+  if (!workspace) return fail(SP_EINVAL, "%s: null workspace", fn);
+  if (workspace_bytes < need)
+    return fail(SP_ERANGE, "%s: workspace holds %lld bytes, %lld needed", fn, (long long)workspace_bytes,
+                (long long)need);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(SP_EINVAL, "%s: workspace must be 256-byte aligned", fn);
+  if (ranges_overlap(workspace, need, q, qb) || ranges_overlap(workspace, need, k, kb) ||
+      ranges_overlap(workspace, need, v, kb) || ranges_overlap(workspace, need, o, qb) ||
+      (lse && ranges_overlap(workspace, need, lse, lb)))
+    return fail(SP_EOVERLAP, "%s: workspace overlaps another buffer", fn);
+  return launch_split_in(fn, q, k, v, o, lse, sq, skv, H, d, scale, nsplit, workspace, stream);
+}
+
+int shard_attn_fwd_split_noalloc(int32_t dtype, const void* q, const void* k, const void* v, void* o, float* lse,
+                                 int64_t sq, int64_t skv, int32_t H, int32_t d, float scale, int32_t nsplit,
+                                 void* stream) {
+  const char* fn = "shard_attn_fwd_split_noalloc";
+  int64_t qb, kb, lb, need;
+  bool skip;
+  if (int rc = check_split(fn, dtype, q, k, v, o, lse, sq, skv, H, d, scale, nsplit, &qb, &kb, &lb, &need, &skip))
+    return rc;
+  if (skip) return ok();
+  if (need > spattn::kScratchBytes)
+    return fail(SP_ERANGE, "%s: the call needs %lld bytes of partials, more than the %lld-byte device scratch", fn,
+                (long long)need, (long long)spattn::kScratchBytes);
+  void* scratch = nullptr;
+  if (hipError_t e = spattn::scratch_address(&scratch)) return hip_fail(e, "scratch address");
+  return launch_split_in(fn, q, k, v, o, lse, sq, skv, H, d, scale, nsplit, scratch, stream);
 }
 
 int shard_attn_fwd_gv(int32_t dtype, const void* q, int32_t W, const void* const* k_shards,

@@ -70,6 +70,13 @@ hipError_t launch_attn_bf16_gv(const void* q, const KvShards& kv, void* o, float
 hipError_t launch_attn_f32_gv(const float* q, const KvShards& kv, float* o, float* lse, int64_t sq, int H, int d,
                               float scale, hipStream_t stream);
 
+// Device scratch of the split attention's allocation-free entry point: one
+// file-scope array per device (kScratchBytes, 256-byte aligned), held until
+// the process ends.  scratch_address() gives the current device's copy; the
+// address is looked up once per device and kept.
+constexpr int64_t kScratchBytes = int64_t(64) << 20;
+hipError_t scratch_address(void** out);
+
 // A HIP launch's grid size is a 32-bit count of work-items per dimension.
 // The host checks every launch of a call against it before enqueuing any.
 constexpr int64_t kMaxItems = (int64_t(1) << 32) - 1;

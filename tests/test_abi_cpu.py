@@ -28,7 +28,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert "shard_attn_fwd" in names and "shard_attn_fwd_gv" in names and len(names) == 18
+    assert "shard_attn_fwd" in names and "shard_attn_fwd_gv" in names and len(names) == 19
     h = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
         assert hasattr(h, n), n
@@ -225,6 +225,24 @@ def test_split_attention_validation():
     assert f(*args, 2, FAKE * 4, need, None) == SP_EOVERLAP         # workspace on top of o
     assert f(0, FAKE, FAKE * 2, FAKE * 3, FAKE * 4, None, 64, 300, 1, 128, 0.08, 2, W, need, None) == SP_EUNSUPPORTED
     assert f(1, FAKE, FAKE * 2, FAKE * 3, FAKE * 4, None, 64, 300, 1, 256, 0.06, 2, W, need, None) == SP_EUNSUPPORTED
+
+
+def test_split_noalloc_validation():
+    """The allocation-free split call validates like the workspace form and refuses
+    partials beyond its 64 MiB device scratch (all before touching a device)."""
+    L = _lib.lib()
+    f = L.shard_attn_fwd_split_noalloc
+    args = (1, FAKE, FAKE * 2, FAKE * 3, FAKE * 4, None, 64, 300, 1, 512, 0.04)
+    assert f(*args, 0, None) == SP_EINVAL                           # nsplit < 1
+    assert f(*args, 6, None) == SP_EINVAL                           # more ranges than 64-key tiles
+    assert f(1, FAKE, FAKE * 2, FAKE * 3, FAKE * 4 + 8, None, 64, 300, 1, 512, 0.04, 2, None) == SP_EINVAL
+    assert f(1, FAKE, FAKE * 2, FAKE * 3, FAKE, None, 64, 300, 1, 512, 0.04, 2, None) == SP_EOVERLAP
+    assert f(0, FAKE, FAKE * 2, FAKE * 3, FAKE * 4, None, 64, 300, 1, 128, 0.08, 2, None) == SP_EUNSUPPORTED
+    # 4,096 queries x 512 channels x 8 ranges = 64 MiB of partials + LSEs: one byte too many
+    assert L.sp_attn_split_workspace(4096, 1, 512, 8) > 64 << 20
+    assert f(1, FAKE, FAKE * 2, FAKE * 3, FAKE * 4, None, 4096, 16384, 1, 512, 0.04, 8, None) == SP_ERANGE
+    assert b"scratch" in L.sp_last_error()
+    assert f(1, FAKE, FAKE * 2, FAKE * 3, FAKE * 4, None, 0, 300, 1, 512, 0.04, 2, None) == 0  # sq == 0
 
 
 def test_av_positions_match_oracle():
