@@ -53,21 +53,99 @@ def traffic_from_profiles(wl_name: str):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(wl, q, k, v, a, b, rows: int):
-    """The fp64 oracle on a bounded sample: `rows` query rows of the rank's shard
-    (all heads) against the full K/V.  Only the oracle's attention is timed;
-    widening the bf16 head slices to fp64 is set-up.  Returns the cpu_baseline object."""
+def host_info() -> dict:
+    """The host the CPU baseline ran on: CPU model, logical CPUs, CPUs this
+    process may use, and the BLAS threads numpy's oracle actually runs with."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        blas = None
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        usable = os.cpu_count()
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "usable_cpus": usable, "blas_threads": blas}
+
+
+def _oracle_share(wl, r, q64, k64, v64):
+    """The oracle's whole share of rank r in float64: RoPE of its Q and K slice,
+    AllGatherV pack + unpack of K and V, attention of its queries against the
+    full K/V, pack + unpack of the W outputs (the other ranks' K rotated and
+    outputs stood in before timing, as on the GPU).  Returns seconds."""
     import numpy as np
 
     import oracle
-    from synth import bf16_bits_to_f32
 
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
-    idx = np.linspace(a, b - 1, rows).astype(np.int64)
+    bounds = oracle.all_shard_bounds(wl.S, wl.W)
+    inner = wl.H * wl.d
+    lens = [b - a for a, b in bounds]
+    k_rot = [oracle.rope_apply(k64[a:b], a, wl.theta) for a, b in bounds]
+    v_sh = [v64[a:b] for a, b in bounds]
+    o_sh = [np.zeros((n, wl.H, wl.d)) for n in lens]
+    counts, displs = oracle.allgatherv_layout(wl.S, wl.W, 1, inner)
+    a, b = bounds[r]
+    t0 = time.perf_counter()
+    qr = oracle.rope_apply(q64[a:b], a, wl.theta)
+    k_rot[r] = oracle.rope_apply(k64[a:b], a, wl.theta)
+    k_full = oracle.varlen_unpack(oracle.varlen_pack(k_rot, counts, displs, np.zeros(sum(counts))), displs, lens, 1,
+                                  inner).reshape(wl.S, wl.H, wl.d)
+    v_full = oracle.varlen_unpack(oracle.varlen_pack(v_sh, counts, displs, np.zeros(sum(counts))), displs, lens, 1,
+                                  inner).reshape(wl.S, wl.H, wl.d)
+    o_sh[r] = oracle.attention(qr, k_full, v_full)[0]
+    oracle.varlen_unpack(oracle.varlen_pack(o_sh, counts, displs, np.zeros(sum(counts))), displs, lens, 1, inner)
+    return time.perf_counter() - t0
+
+
+def _gpu_share_ms(wl, r, qd, kd, vd, reps: int = 5) -> float:
+    """Event-timed whole share of rank r on the GPU (median of reps)."""
+    import torch
+
+    from sequence_dit_attention_amd.pipeline import RankShare
+
+    share = RankShare(wl.S, wl.W, r, wl.H, wl.d, qd.dtype, wl.theta, qd.device)
+    share.set_inputs(qd, kd, vd)
+    share.step()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        share.step()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    return sorted(times)[len(times) // 2]
+
+
+def cpu_baseline(wl, q, k, v, a, b, rows: int, gpu_attn_ms: float, gpu_pack_ms: float, gpu_rope_ms: float):
+    """The float64 oracle on the host, beside the GPU numbers of the same run.
+
+    Headline (`value`): the oracle's attention on a bounded sample of the
+    benchmark workload -- `rows` query rows of the rank's shard (first and last
+    rows, both sides of 128-row tile edges, the rest drawn at random) x all
+    heads against the full K/V -- in TFLOP/s, extrapolated to the shard.
+    `rows_detail` adds the oracle's whole rank share, timed in full, of the tiny
+    float32 workload and of the uneven bf16 workload (all four ranks of each),
+    each beside the GPU's event-timed share, and the oracle's K pack and RoPE
+    at the benchmark size.  Widening bf16 to float64 is set-up, not timed."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from synth import bf16_bits_to_f32, gen_qkv, get_workload, sample_rows
+
+    info = host_info()
+    idx = a + sample_rows(b - a, rows, seed=17)
     qrows = bf16_bits_to_f32(q[idx]).astype(np.float64)
     spent = 0.0
     for h in range(wl.H):
@@ -76,11 +154,40 @@ def cpu_baseline(wl, q, k, v, a, b, rows: int):
         t0 = time.perf_counter()
         oracle.attention(qrows[:, h:h + 1, :], kh, vh)
         spent += time.perf_counter() - t0
-    flops = 4.0 * rows * wl.S * wl.H * wl.d
+    n = len(idx)
+    flops = 4.0 * n * wl.S * wl.H * wl.d
+    cpu_tflops = flops / spent / 1e12
+    shard_s = spent * (b - a) / n
+    detail = [{"workload": wl.name, "what": f"attention of the rank-{wl.ranks[0]} shard ({b - a} queries x {wl.H} "
+                                           f"heads x {wl.S} keys)",
+               "kind": f"extrapolated from {n} rows", "cpu_s": shard_s, "gpu_ms": gpu_attn_ms,
+               "gpu_over_cpu": shard_s * 1e3 / gpu_attn_ms}]
 
-    # The data-movement rows beside it: the oracle's AllGatherV pack of the four
-    # K shards (the whole tensor, bf16 bit patterns) and its RoPE on 2,048
-    # tokens of the rank's Q slice (float64), as algorithmic GB/s of the bf16 data.
+    # The oracle's whole share, in full, on the two workloads small enough for it.
+    def widen(x, dt):
+        return (bf16_bits_to_f32(x) if dt == "bf16" else x).astype(np.float64)
+
+    def dev(x, dt):
+        if dt == "f32":
+            return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(torch.bfloat16)
+
+    for name in ("tiny_f32", "uneven_bf16"):
+        w = get_workload(name)
+        wq, wk, wv = gen_qkv(w)
+        q64, k64, v64 = widen(wq, w.dtype), widen(wk, w.dtype), widen(wv, w.dtype)
+        ranks = list(range(w.W))   # every rank of the workload, one after another
+        cpu_s = sum(_oracle_share(w, r, q64, k64, v64) for r in ranks)
+        qd, kd, vd = dev(wq, w.dtype), dev(wk, w.dtype), dev(wv, w.dtype)
+        gpu_ms = sum(_gpu_share_ms(w, r, qd, kd, vd) for r in ranks)
+        log(f"CPU oracle, {name}: {cpu_s:.1f} s for ranks {ranks} (GPU {gpu_ms:.3f} ms)")
+        detail.append({"workload": name, "what": f"whole share (RoPE, K/V pack + unpack, attention, output "
+                                                  f"concat) of ranks {ranks}, summed",
+                       "kind": "full", "cpu_s": cpu_s, "gpu_ms": gpu_ms, "gpu_over_cpu": cpu_s * 1e3 / gpu_ms})
+
+    # Data movement at the benchmark size: the oracle's AllGatherV pack of the
+    # four K shards (the whole tensor, bf16 bit patterns) and its RoPE of 2,048
+    # tokens of the rank's Q slice, in algorithmic GB/s of the bf16 data.
     bounds = [oracle.shard_bounds(wl.S, wl.W, r) for r in range(wl.W)]
     inner = wl.H * wl.d
     counts, displs = oracle.allgatherv_layout(wl.S, wl.W, 1, inner)
@@ -96,14 +203,20 @@ def cpu_baseline(wl, q, k, v, a, b, rows: int):
     t_rope = time.perf_counter() - t0
     pack_b = 2.0 * wl.S * inner * k.itemsize
     rope_b = 2.0 * nr * inner * 2
-    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{rows} query rows x {wl.H} heads of the rank-{wl.ranks[0]} shard against the full "
-                      f"{wl.S}-token K/V (fp64 numpy oracle attention, {spent:.1f} s)",
-            "other_rows": {
-                "pack_kv_gbs": pack_b / t_pack / 1e9,
-                "pack_sample": f"the {wl.W} K shards ({pack_b / 2e9:.2f} GB of bf16) into one flat buffer, {t_pack:.2f} s",
-                "rope_gbs": rope_b / t_rope / 1e9,
-                "rope_sample": f"{nr} tokens x {wl.H} heads of the rank's Q slice in float64, {t_rope:.2f} s"}}
+    gpu_pack_gbs = 2 * pack_b / (gpu_pack_ms * 1e-3) / 1e9   # the GPU step packs K and V
+    gpu_rope_gbs = 2 * 2.0 * (b - a) * inner * 2 / (gpu_rope_ms * 1e-3) / 1e9   # RoPE of Q and K
+    detail.append({"workload": wl.name, "what": f"AllGatherV pack of the {wl.W} K shards ({pack_b / 2e9:.2f} GB)",
+                   "kind": "full", "cpu_gbs": pack_b / t_pack / 1e9, "gpu_gbs": gpu_pack_gbs,
+                   "gpu_over_cpu": gpu_pack_gbs / (pack_b / t_pack / 1e9)})
+    detail.append({"workload": wl.name, "what": f"RoPE of {nr} tokens x {wl.H} heads of the rank's Q slice",
+                   "kind": "sample", "cpu_gbs": rope_b / t_rope / 1e9, "gpu_gbs": gpu_rope_gbs,
+                   "gpu_over_cpu": gpu_rope_gbs / (rope_b / t_rope / 1e9)})
+    gpu_tflops = flops / n * (b - a) / (gpu_attn_ms * 1e-3) / 1e12
+    return {"value": cpu_tflops, "unit": "TFLOP/s", "cores": info["blas_threads"] or info["usable_cpus"],
+            "kind": "oracle",
+            "sample": f"{n} query rows x {wl.H} heads of the rank-{wl.ranks[0]} shard against the full {wl.S}-token "
+                      f"K/V (fp64 numpy oracle attention, {spent:.1f} s)",
+            "host": info, "gpu_over_cpu": gpu_tflops / cpu_tflops, "rows_detail": detail}
 
 
 def main() -> int:
@@ -112,8 +225,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="p768_15s_w4")
-    ap.add_argument("--cpu-rows", type=int, default=400,
-                    help="query rows in the CPU-oracle sample, about 10-15 s of host work (0: skip)")
+    ap.add_argument("--cpu-rows", type=int, default=512,
+                    help="query rows in the CPU-oracle sample, about 15-20 s of host work (0: skip)")
     ap.add_argument("--vae-steps", type=int, default=3, help="timed steps of the VAE block-split share (0: skip)")
     ap.add_argument("--gf-steps", type=int, default=2,
                     help="steps of the gather-free variant timed after the headline steps (0: skip)")
@@ -320,7 +433,8 @@ def main() -> int:
     }
     if args.cpu_rows > 0:
         log(f"CPU oracle baseline on {args.cpu_rows} rows")
-        out["cpu_baseline"] = cpu_baseline(wl, q, k, v, share.a, share.b, args.cpu_rows)
+        out["cpu_baseline"] = cpu_baseline(wl, q, k, v, share.a, share.b, args.cpu_rows, per["attn"],
+                                           per["pack_kv"], per["rope"])
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
