@@ -228,6 +228,9 @@ def main() -> int:
     ap.add_argument("--cpu-rows", type=int, default=512,
                     help="query rows in the CPU-oracle sample, about 15-20 s of host work (0: skip)")
     ap.add_argument("--vae-steps", type=int, default=3, help="timed steps of the VAE block-split share (0: skip)")
+    ap.add_argument("--calib-copy-gib", type=float, default=0.0,
+                    help="before timing, one plain elementwise copy (torch neg) of this many GiB of bf16, the known-size "
+                         "kernel the HBM counters of a profile are calibrated on (0: none)")
     ap.add_argument("--gf-steps", type=int, default=2,
                     help="steps of the gather-free variant timed after the headline steps (0: skip)")
     args = ap.parse_args()
@@ -268,6 +271,22 @@ def main() -> int:
     for _ in range(args.warmup):
         share.step()
     torch.cuda.synchronize()
+
+    calib = None
+    if args.calib_copy_gib > 0:
+        n = int(args.calib_copy_gib * (1 << 30)) // 2
+        src = torch.ones(n, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.neg(src, out=dst)
+        e1.record()
+        torch.cuda.synchronize()
+        calib = {"kernel": "torch neg (vectorized elementwise)", "bytes_read": 2 * n, "bytes_written": 2 * n,
+                 "ms": e0.elapsed_time(e1)}
+        del src, dst
+        log(f"calibration copy: {4 * n / 2**30:.2f} GiB moved in {calib['ms']:.3f} ms")
 
     stages = ["rope", "pack_kv", "unpack_kv", "attn", "concat_out"]
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
@@ -431,6 +450,8 @@ def main() -> int:
         "qk_norm_rope": qnr,
         "vae_block_attention": vae,
     }
+    if calib is not None:
+        out["calib_copy"] = calib
     if args.cpu_rows > 0:
         log(f"CPU oracle baseline on {args.cpu_rows} rows")
         out["cpu_baseline"] = cpu_baseline(wl, q, k, v, share.a, share.b, args.cpu_rows, per["attn"],
