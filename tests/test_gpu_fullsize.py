@@ -4,7 +4,8 @@ The whole rank share (RoPE, K/V AllGatherV pack + unpack, attention, output
 concat) runs through sequence_dit_attention_amd.pipeline.RankShare at the
 workloads' real shapes.  The fp64 oracle is too slow for every output at these
 sizes, so it is evaluated on sampled query rows (first/last rows, both sides
-of 128-row tile edges, random rows) for every head; pack/unpack are checked
+of 128-row tile edges, both sides of 256-row work-group boundaries spread over the
+shard, the final partial work-group, random rows) for every head; pack/unpack are checked
 bit-exactly on sampled elements and by the exact round-trip property, RoPE on
 the sampled rows.
 """
@@ -57,7 +58,13 @@ def test_fullsize_rank_share(name):
     share.step()
     torch.cuda.synchronize()
     a, b = share.a, share.b
-    rows = sample_rows(b - a, 32, seed=wl.seed)
+    # 32 sampled rows (first/last, 128-row tile edges, random), plus both sides of 24 work-group
+    # boundaries (every 256 query rows form one work-group) spread evenly over the shard, and the
+    # first and last rows of the final, partial work-group
+    n = b - a
+    wg = np.unique(np.linspace(1, max(1, (n - 1) // 256), 24).astype(np.int64)) * 256
+    edges = np.concatenate([wg - 1, wg, [((n - 1) // 256) * 256, n - 1]])
+    rows = np.unique(np.concatenate([sample_rows(n, 32, seed=wl.seed), edges[(edges >= 0) & (edges < n)]]))
     rows_abs = rows + a
     _log(f"{name}: GPU done; oracle on {len(rows)} rows x {wl.H} heads")
 
