@@ -787,18 +787,26 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const uint16_t* __r
     tile_barrier<kBatch * (kLead - 1)>();
     if constexpr (GV) {
       const int jk = t + kLead + 1, jv = t + kLead;
-      if (jk >= kcross) {
-        load_sharded(kl, kv.k, kcur, jk, kslot(jk));
-        kaddr = reinterpret_cast<uint64_t>(kcur.p) + uint64_t(int64_t(jk) * kBN - kcur.s0) * uint64_t(rowbytes);
-        kcross = kcur.s1 / kBN;
+      // One test for both streams, expected false: the common path is the
+      // gathered one (two loads from advancing addresses), the cursor code
+      // stays out of line.
+      if (__builtin_expect(jk >= kcross || jv >= vcross, 0)) {
+        if (jk >= kcross) {
+          load_sharded(kl, kv.k, kcur, jk, kslot(jk));
+          kaddr = reinterpret_cast<uint64_t>(kcur.p) + uint64_t(int64_t(jk) * kBN - kcur.s0) * uint64_t(rowbytes);
+          kcross = kcur.s1 / kBN;
+        } else {
+          kl.load_at(kaddr, kslot(jk), wave);
+        }
+        if (jv >= vcross) {
+          load_sharded(vl, kv.v, vcur, jv, vslot(jv));
+          vaddr = reinterpret_cast<uint64_t>(vcur.p) + uint64_t(int64_t(jv) * kBN - vcur.s0) * uint64_t(rowbytes);
+          vcross = vcur.s1 / kBN;
+        } else {
+          vl.load_at(vaddr, vslot(jv), wave);
+        }
       } else {
         kl.load_at(kaddr, kslot(jk), wave);
-      }
-      if (jv >= vcross) {
-        load_sharded(vl, kv.v, vcur, jv, vslot(jv));
-        vaddr = reinterpret_cast<uint64_t>(vcur.p) + uint64_t(int64_t(jv) * kBN - vcur.s0) * uint64_t(rowbytes);
-        vcross = vcur.s1 / kBN;
-      } else {
         vl.load_at(vaddr, vslot(jv), wave);
       }
     } else {
