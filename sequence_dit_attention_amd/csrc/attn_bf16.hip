@@ -615,8 +615,11 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const uint16_t* __r
   TileLoader<G, true> vl;
   kl.init(wave, lane, rowbytes);
   vl.init(wave, lane, rowbytes);
-  auto kslot = [&](int j) { return smem + (j % kKSlots) * G::kTileB; };
-  auto vslot = [&](int j) { return vbase + (j % kVSlots) * G::kVTileB; };
+  // Tile indices are never negative: unsigned remainders (a mask for a power
+  // of two slot count) instead of the signed sequence the compiler must emit
+  // wherever it cannot prove the index non-negative.
+  auto kslot = [&](int j) { return smem + (unsigned(j) % unsigned(kKSlots)) * G::kTileB; };
+  auto vslot = [&](int j) { return vbase + (unsigned(j) % unsigned(kVSlots)) * G::kVTileB; };
   // Tile indices past the end are clamped: those loads land in slots no live
   // tile uses and keep every batch the same size for the vmcnt accounting.
   // Sharded K/V: a cursor per stream (K, V) follows the shard that holds the
@@ -781,41 +784,51 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const uint16_t* __r
   // Sharded K/V: tiles below kcross (vcross) lie inside the stream's current
   // shard and advance from kaddr (vaddr) like gathered ones; a tile at or
   // past it goes through the cursor, which also resets the address and the
-  // crossing point.
+  // crossing point.  The steady loop runs between crossing points, so its
+  // body holds no cursor test at all.
   int kcross = 0, vcross = 0;
-  for (; t <= nT - 3 - kLead; ++t) {
-    tile_barrier<kBatch * (kLead - 1)>();
-    if constexpr (GV) {
-      const int jk = t + kLead + 1, jv = t + kLead;
-      // One test for both streams, expected false: the common path is the
-      // gathered one (two loads from advancing addresses), the cursor code
-      // stays out of line.
-      if (__builtin_expect(jk >= kcross || jv >= vcross, 0)) {
-        if (jk >= kcross) {
-          load_sharded(kl, kv.k, kcur, jk, kslot(jk));
-          kaddr = reinterpret_cast<uint64_t>(kcur.p) + uint64_t(int64_t(jk) * kBN - kcur.s0) * uint64_t(rowbytes);
-          kcross = kcur.s1 / kBN;
-        } else {
-          kl.load_at(kaddr, kslot(jk), wave);
-        }
-        if (jv >= vcross) {
-          load_sharded(vl, kv.v, vcur, jv, vslot(jv));
-          vaddr = reinterpret_cast<uint64_t>(vcur.p) + uint64_t(int64_t(jv) * kBN - vcur.s0) * uint64_t(rowbytes);
-          vcross = vcur.s1 / kBN;
-        } else {
-          vl.load_at(vaddr, vslot(jv), wave);
-        }
-      } else {
-        kl.load_at(kaddr, kslot(jk), wave);
-        vl.load_at(vaddr, vslot(jv), wave);
-      }
-    } else {
+  const int tsteady = nT - 2 - kLead;  // steady tiles: t < tsteady
+  for (;;) {
+    // Steady run: with sharded K/V it stops before the first tile whose loads
+    // reach a crossing point (K tile t+kLead+1 >= kcross or V tile t+kLead >=
+    // vcross), so its body is the gathered one.
+    int tend = tsteady;
+    if constexpr (GV) tend = min(tend, min(kcross - kLead - 1, vcross - kLead));
+    for (; t < tend; ++t) {
+      tile_barrier<kBatch * (kLead - 1)>();
       kl.load_at(kaddr, kslot(t + kLead + 1), wave);
       vl.load_at(vaddr, vslot(t + kLead), wave);
+      kaddr += tb;
+      vaddr += tb;
+      tile_steps(t, F{}, F{});
     }
-    kaddr += tb;
-    vaddr += tb;
-    tile_steps(t, F{}, F{});
+    if constexpr (!GV) {
+      break;
+    } else {
+      if (t >= tsteady) break;
+      // A crossing tile: the cursor loads it and resets the stream's address
+      // and crossing point.
+      tile_barrier<kBatch * (kLead - 1)>();
+      const int jk = t + kLead + 1, jv = t + kLead;
+      if (jk >= kcross) {
+        load_sharded(kl, kv.k, kcur, jk, kslot(jk));
+        kaddr = reinterpret_cast<uint64_t>(kcur.p) + uint64_t(int64_t(jk) * kBN - kcur.s0) * uint64_t(rowbytes);
+        kcross = kcur.s1 / kBN;
+      } else {
+        kl.load_at(kaddr, kslot(jk), wave);
+      }
+      if (jv >= vcross) {
+        load_sharded(vl, kv.v, vcur, jv, vslot(jv));
+        vaddr = reinterpret_cast<uint64_t>(vcur.p) + uint64_t(int64_t(jv) * kBN - vcur.s0) * uint64_t(rowbytes);
+        vcross = vcur.s1 / kBN;
+      } else {
+        vl.load_at(vaddr, vslot(jv), wave);
+      }
+      kaddr += tb;
+      vaddr += tb;
+      tile_steps(t, F{}, F{});
+      ++t;
+    }
   }
   for (; t < nT - 2; ++t) {  // the next tile is not the last one: no masking
     tile_barrier<kBatch * (kLead - 1)>();
