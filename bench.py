@@ -227,7 +227,9 @@ def main() -> int:
     ap.add_argument("--workload", default="p768_15s_w4")
     ap.add_argument("--cpu-rows", type=int, default=512,
                     help="query rows in the CPU-oracle sample, about 15-20 s of host work (0: skip)")
-    ap.add_argument("--vae-steps", type=int, default=3, help="timed steps of the VAE block-split share (0: skip)")
+    ap.add_argument("--vae-steps", type=int, default=20, help="timed steps of the VAE block-split share (0: skip)")
+    ap.add_argument("--vae-eager-only", action="store_true",
+                    help="time the VAE share's eager steps only (no graph replay), e.g. under counter collection")
     ap.add_argument("--calib-copy-gib", type=float, default=0.0,
                     help="before timing, one plain elementwise copy (torch neg) of this many GiB of bf16, the known-size "
                          "kernel the HBM counters of a profile are calibrated on (0: none)")
@@ -390,12 +392,14 @@ def main() -> int:
     vae = None
     if args.vae_steps > 0:
         from sequence_dit_attention_amd.pipeline import VaeBlockShare
-        vs = VaeBlockShare(128, 128, 512, 2, 2, 0, nsplit=4)
+        vs = VaeBlockShare(128, 128, 512, 2, 2, 0, nsplit=8)
         gq, gk, gv = (gen_tensor(wl.seed + 100, t, vs.n, 1, vs.C, "bf16") for t in range(3))
         dev_bf16 = lambda a: torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16).view(128, 128, 512)
         vs.set_inputs(dev_bf16(gq), dev_bf16(gk), dev_bf16(gv))
         vs.step()
         torch.cuda.synchronize()
+        eager_o = vs.o.clone()
+        # Eager steps, one event per phase (host launch gaps included).
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.vae_steps)]
         for i in range(args.vae_steps):
             ev[i][0].record()
@@ -408,12 +412,31 @@ def main() -> int:
         torch.cuda.synchronize()
         vms = [sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.vae_steps)) / args.vae_steps
                for j in range(3)]
+        # The same step replayed as a HIP graph (all five launches issued at once).
+        graph_ms, replay_same = None, None
+        if not args.vae_eager_only:
+            graph = vs.capture()
+            graph.replay()
+            torch.cuda.synchronize()
+            g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            g0.record()
+            for _ in range(args.vae_steps):
+                graph.replay()
+            g1.record()
+            torch.cuda.synchronize()
+            graph_ms = g0.elapsed_time(g1) / args.vae_steps
+            replay_same = bool(torch.equal(vs.o.view(torch.int16), eager_o.view(torch.int16)))
         va_tf = vs.attn_flops() / (vms[1] * 1e-3) / 1e12
         vae = {"workload": "vae_128x128_c512_blocks2x2_p0", "sq": vs.m, "skv": vs.n, "d": vs.C, "nsplit": vs.nsplit,
-               "ms_per_step": sum(vms), "gather_kv_ms": vms[0], "attn_ms": vms[1], "place_out_ms": vms[2],
+               "ms_per_step": graph_ms if graph_ms is not None else sum(vms),
+               "launch": "eager" if graph_ms is None else "hip_graph", "graph_equals_eager": replay_same,
+               "eager_ms_per_step": sum(vms), "gather_kv_ms": vms[0], "attn_ms": vms[1], "place_out_ms": vms[2],
                "attn_tflops": va_tf, "attn_frac_mfma_peak": va_tf / PEAK_BF16_TFLOPS,
                "copy_gbs": vs.copy_bytes() / ((vms[0] + vms[2]) * 1e-3) / 1e9}
-        log(f"VAE block share: {sum(vms):.3f} ms (attention {vms[1]:.3f} ms, {va_tf:.0f} TFLOP/s)")
+        if replay_same is False:
+            raise RuntimeError("VAE share: graph replay differs from the eager step")
+        log(f"VAE block share: {vae['ms_per_step']:.3f} ms per step ({vae['launch']}), {sum(vms):.3f} ms eager "
+            f"(attention {vms[1]:.3f} ms, {va_tf:.0f} TFLOP/s)")
 
     flops = share.attn_flops()
     attn_tflops = flops / (per["attn"] * 1e-3) / 1e12

@@ -232,6 +232,21 @@ int tile_unpack(int32_t dtype, const void* flat, int64_t flat_elems, int64_t Hh,
                 int32_t pc, void* raster, void* stream);
 
 /*
+ * tile_pack_n -- tile_pack of n rasters of one shape in one batch of copies.
+ * Section VAE并行优化 gathers the K and V blocks of every process before the
+ * attention; this packs both (or any n <= 16 tensors) with one launch instead
+ * of one per tensor: flats[a] <- blocks of rasters[a], each exactly as
+ * tile_pack.
+ *   rasters, flats  host arrays of n device pointers (the caller keeps them;
+ *                   read during the call only)
+ *   flat_elems      capacity of every flats[a], in elements
+ * Errors: those of tile_pack, plus SP_EINVAL (n outside [1, 16], null arrays)
+ * and SP_EOVERLAP (a flat overlaps any raster or another flat).
+ */
+int tile_pack_n(int32_t dtype, int32_t n, const void* const* rasters, int64_t Hh, int64_t Ww, int64_t C, int32_t pr,
+                int32_t pc, void* const* flats, int64_t flat_elems, void* stream);
+
+/*
  * qk_norm_rope -- per-head RMSNorm of q or k fused with the rotary embedding.
  * Page "NPU HunyuanImage-3.0模型推理优化实践", section 计算分解: after the merged
  * QKV projection the query and key heads are normalised and then rotated

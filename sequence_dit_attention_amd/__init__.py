@@ -22,6 +22,7 @@ from .api import (  # noqa: F401
     sp_shard_bounds,
     sp_tile_bounds,
     tile_pack,
+    tile_pack_n,
     tile_unpack,
     varlen_pack,
     varlen_unpack,

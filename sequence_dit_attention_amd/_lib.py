@@ -25,6 +25,8 @@ SIGNATURES = [
     ("sp_tile_bounds", ctypes.c_int, [_I64, _I64, _I32, _I32, _I32, _PI64]),
     ("tile_pack", ctypes.c_int, [_I32, _VP, _I64, _I64, _I64, _I32, _I32, _VP, _I64, _VP]),
     ("tile_unpack", ctypes.c_int, [_I32, _VP, _I64, _I64, _I64, _I64, _I32, _I32, _VP, _VP]),
+    ("tile_pack_n", ctypes.c_int, [_I32, _I32, ctypes.POINTER(_VP), _I64, _I64, _I64, _I32, _I32,
+                                   ctypes.POINTER(_VP), _I64, _VP]),
     ("shard_attn_fwd_split", ctypes.c_int, [_I32, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I32, _I32, ctypes.c_float,
                                             _I32, _VP, _I64, _VP]),
     ("shard_attn_fwd_split_noalloc", ctypes.c_int, [_I32, _VP, _VP, _VP, _VP, _VP, _I64, _I64, _I32, _I32,

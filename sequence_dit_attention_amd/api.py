@@ -181,6 +181,28 @@ def tile_pack(raster: torch.Tensor, pr: int, pc: int, flat: torch.Tensor | None 
     return flat
 
 
+def tile_pack_n(rasters, pr: int, pc: int, flats=None) -> list:
+    """tile_pack of several rasters [Hh, Ww, C] of one shape and dtype in one batch of copies."""
+    rasters = list(rasters)
+    if not rasters or any(r.dim() != 3 for r in rasters):
+        raise ValueError("rasters must be a non-empty list of [Hh, Ww, C]")
+    Hh, Ww, C = rasters[0].shape
+    if any(r.shape != rasters[0].shape or r.dtype != rasters[0].dtype for r in rasters):
+        raise ValueError("rasters must share shape and dtype")
+    if flats is None:
+        flats = [torch.empty(Hh * Ww, C, dtype=r.dtype, device=r.device) for r in rasters]
+    flats = list(flats)
+    if len(flats) != len(rasters) or any(f.dtype != rasters[0].dtype for f in flats):
+        raise ValueError("one flat per raster, of the rasters' dtype")
+    n = len(rasters)
+    cap = min(f.numel() for f in flats)
+    rp = (ctypes.c_void_p * n)(*[_dev(r, "raster") for r in rasters])
+    fp = (ctypes.c_void_p * n)(*[_dev(f, "flat") for f in flats])
+    check("tile_pack_n", lib().tile_pack_n(_dtype_code(rasters[0]), n, rp, Hh, Ww, C, pr, pc, fp, cap,
+                                           _stream(rasters[0])))
+    return flats
+
+
 def tile_unpack(flat: torch.Tensor, Hh: int, Ww: int, pr: int, pc: int,
                 raster: torch.Tensor | None = None) -> torch.Tensor:
     """Put the blocks of flat (process order, each row-major, C channels) back into raster [Hh, Ww, C]."""

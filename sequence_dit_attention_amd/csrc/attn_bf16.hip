@@ -41,12 +41,9 @@
 //  * Work-groups are ordered head-major, so at any time all XCDs work on the
 //    same head: its K+V (188 MB at 367k tokens) stays in the 256 MB Infinity
 //    Cache and each XCD's L2 serves its co-resident query tiles.
-//  * Head size 512 (the single-head attention over the channels of a VAE
-//    feature map, page "NPU HunyuanImage-3.0模型推理优化实践", VAE并行优化):
-//    one 32-query block per wave (128 rows per work-group), 32-key tiles,
-//    and each work-group produces 256 of the 512 output columns, so a lane's
-//    O^T accumulators (128 registers) and Q fragments (128) fit; the two
-//    column halves are separate work-groups that both form the full scores.
+//  * Head sizes 64 and 128.  Head size 512 (the VAE's single-head attention)
+//    has a kernel of its own (attn_d512.hip), since its accumulators and Q
+//    fragments do not fit this layout.
 // Per output row the arithmetic depends only on that query row and on K/V in
 // a fixed key order, so results are deterministic and independent of sq and
 // of the row's position inside a tile.
@@ -95,9 +92,6 @@ constexpr int kRA = SPATTN_RA;
 #ifndef SPATTN_EARLY
 #define SPATTN_EARLY 4  // of the 8 words per query block, those made one step early
 #endif
-#ifndef SPATTN_LEAD512
-#define SPATTN_LEAD512 1  // tiles loaded ahead for head size 512
-#endif
 #ifndef SPATTN_BN
 #define SPATTN_BN 64  // keys per tile (head sizes 64, 128)
 #endif
@@ -106,34 +100,30 @@ constexpr float kTau = 8.0f;           // lazy-rescale threshold (log2 units)
 constexpr float kCheck = 256.0f;       // 2^kTau: a lane's block sum above it triggers the reference check
 constexpr float kLn2 = 0.69314718055994531f;
 
-// Shape of the kernel for head size D.  D <= 128: two 32-query blocks per
-// wave (QB), 64-key tiles, every output column.  D = 512: a work-group
-// produces DV = 256 of the output columns (the O^T accumulator of a 32-query
-// block over all 512 would take every register a lane has), one query block
-// per wave, and 32-key tiles (64 keys x 1 KiB rows would not leave room for
-// the pipeline's slots in the 160 KiB of LDS).
-template <int D, int DV = D>
+// Shape of the kernel for head size D (64 or 128): two 32-query blocks per
+// wave (QB), 64-key tiles, every output column.
+template <int D>
 struct Geo {
+  static_assert(D == 64 || D == 128, "head sizes 64 and 128");
   static constexpr int kD = D;
-  static constexpr int kDV = DV;
-  static constexpr int QB = D <= 128 ? SPATTN_QB : 1;     // 32-query MFMA blocks per wave
+  static constexpr int QB = SPATTN_QB;                    // 32-query MFMA blocks per wave
   static constexpr int BM = kWaves * 32 * QB;             // query rows per work-group
-  static constexpr int kBN = D <= 128 ? SPATTN_BN : 32;   // keys per tile
+  static constexpr int kBN = SPATTN_BN;                   // keys per tile
   static constexpr int kSteps = kBN / 32;                 // 32-key steps per tile
   static_assert(kSteps == 1 || kSteps % 2 == 0, "the two S^T register sets alternate within a tile");
   // Probability words per query block made one step early, under the P*V
   // MFMAs of the previous step (the part of a step that has no other VALU work).
-  static constexpr int kEarly = D <= 128 ? SPATTN_EARLY : 0;
+  static constexpr int kEarly = SPATTN_EARLY;
   // With two or more steps per tile, the first K fragments of the block after
   // next are read ahead at the end of a step; with one step that block is two
   // tiles ahead and the fragments are read at the start of the step instead.
   static constexpr bool kPrefetch = kSteps >= 2;
   static constexpr int kCh = D / 8;                       // 16-byte chunks per K row
-  static constexpr int kVCh = DV / 8;                     // 16-byte chunks per V row (its DV columns)
+  static constexpr int kVCh = D / 8;                      // 16-byte chunks per V row
   static constexpr int kDC = D / 16;                      // k-steps of the Q.K MFMA
-  static constexpr int kND = DV / 32;                     // 32-row d-blocks of O^T
+  static constexpr int kND = D / 32;                      // 32-row d-blocks of O^T
   static constexpr int kRowB = D * 2;                     // bytes per K row
-  static constexpr int kVRowB = DV * 2;                   // bytes per V row in LDS
+  static constexpr int kVRowB = D * 2;                    // bytes per V row in LDS
   static constexpr int kTileB = kBN * kRowB;              // bytes per K tile
   static constexpr int kVTileB = kBN * kVRowB;            // bytes per V tile
   static constexpr int kLoads = kTileB / (kThreads * 16); // LDS-direct loads per lane per K tile
@@ -142,7 +132,7 @@ struct Geo {
   // t+2 .. t+1+kLead loading.  V: tile t read, t+1 .. t+kLead loading.  Slot
   // counts are rounded up to powers of two (slot indices become masks) when
   // that still fits the 160 KiB of LDS.
-  static constexpr int kLead = D <= 128 ? SPATTN_LEAD : SPATTN_LEAD512;  // K/V tiles in flight ahead of the one in use
+  static constexpr int kLead = SPATTN_LEAD;               // K/V tiles in flight ahead of the one in use
   static constexpr int kKNeed = kLead + (kSteps >= 2 ? 2 : 1);
   static constexpr int kVNeed = kLead + 1;
   static constexpr bool kPow2 = pow2_ceil(kKNeed) * kTileB + pow2_ceil(kVNeed) * kVTileB <= 160 * 1024;
@@ -557,15 +547,14 @@ using KvArg = typename std::conditional<GV, KvShards, KvFlat>::type;
 // work-group index; each work-group writes its float32 O normalised over its
 // own keys and that range's LSE (opart [nsplit, sq, H, D], lse [nsplit, H, sq])
 // for merge_kernel to combine.
-template <int D, int DV, bool GV, bool SPLIT>
+template <int D, bool GV, bool SPLIT>
 __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const uint16_t* __restrict__ q, const KvArg<GV> kv,
                                                              uint16_t* __restrict__ o, float* __restrict__ lse,
                                                              int sq, int skv_all, int H, float c, int nqt,
                                                              int nsplit, float* __restrict__ opart) {
-  using G = Geo<D, DV>;
+  using G = Geo<D>;
   constexpr int QB = G::QB, BM = G::BM, kBN = G::kBN, kSteps = G::kSteps;
   constexpr int kKSlots = G::kKSlots, kVSlots = G::kVSlots, kLead = G::kLead;
-  constexpr int kNCB = D / DV;  // output column blocks per head
   static_assert(kKSlots * G::kTileB + kVSlots * G::kVTileB <= 160 * 1024, "K/V slots exceed the LDS");
   // K tile j lives in slot j mod kKSlots, V tile j in slot j mod kVSlots.
   __shared__ __attribute__((aligned(1024))) char smem[kKSlots * G::kTileB + kVSlots * G::kVTileB];
@@ -573,20 +562,18 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const uint16_t* __r
   constexpr unsigned kBatch = G::kLoads + G::kVLoads;  // LDS-direct loads per wave per tile (K and V)
 
   // Head-major order: consecutive work-groups (spread over all XCDs) share a
-  // head; within a head, column block cb of every query tile, then the next.
+  // head.
   const int L = blockIdx.x;
-  int hc, qt, sp = 0;
-  if constexpr (SPLIT) {  // query tiles fastest, then key ranges, then (head, column block)
+  int h, qt, sp = 0;
+  if constexpr (SPLIT) {  // query tiles fastest, then key ranges, then heads
     qt = L % nqt;
     const int rest = L / nqt;
     sp = rest % nsplit;
-    hc = rest / nsplit;
+    h = rest / nsplit;
   } else {
-    hc = L / nqt;
-    qt = L - hc * nqt;
+    h = L / nqt;
+    qt = L - h * nqt;
   }
-  const int h = hc / kNCB;
-  const int cb = hc - h * kNCB;
   // This work-group's keys [k0, k0 + skv): all of them, or key range sp.
   int k0 = 0, skv = skv_all;
   if constexpr (SPLIT) {
@@ -606,7 +593,7 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const uint16_t* __r
   const uint16_t* vh = nullptr;
   if constexpr (!GV) {
     kh = kv.k + int64_t(k0) * rowstride + int64_t(h) * D;
-    vh = kv.v + int64_t(k0) * rowstride + int64_t(h) * D + cb * DV;
+    vh = kv.v + int64_t(k0) * rowstride + int64_t(h) * D;
   }
   const int nT = (skv + kBN - 1) / kBN;
   const bool ragged = (skv % kBN) != 0;
@@ -633,11 +620,11 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const uint16_t* __r
     const char* p;   // its base pointer, offset to the stream's columns of head h
     int64_t off;     // that byte offset inside a token row
   };
-  const int64_t hoff = int64_t(h) * D * 2, hoff_v = hoff + int64_t(cb) * DV * 2;
+  const int64_t hoff = int64_t(h) * D * 2;  // byte offset of head h inside a token row
   Cursor kcur{0, 0, 0, nullptr, 0}, vcur{0, 0, 0, nullptr, 0};
   if constexpr (GV) {
     kcur = Cursor{0, 0, int(kv.start[1]), static_cast<const char*>(kv.k[0]) + hoff, hoff};
-    vcur = Cursor{0, 0, int(kv.start[1]), static_cast<const char*>(kv.v[0]) + hoff_v, hoff_v};
+    vcur = Cursor{0, 0, int(kv.start[1]), static_cast<const char*>(kv.v[0]) + hoff, hoff};
   }
   auto load_sharded = [&](const auto& ld, const void* const* ptr, Cursor& cu, int tile, char* lds) {
     if constexpr (GV) {
@@ -854,7 +841,7 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const uint16_t* __r
     const float inv = 1.f / lt;
     const int row = qrow0 + qb * 32 + col;
     if (SPLIT && row < sq) {
-      float* dst = opart + (int64_t(sp) * sq + row) * rowstride + int64_t(h) * D + cb * DV;
+      float* dst = opart + (int64_t(sp) * sq + row) * rowstride + int64_t(h) * D;
 #pragma unroll
       for (int db = 0; db < G::kND; ++db)
 #pragma unroll
@@ -863,9 +850,9 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const uint16_t* __r
           *reinterpret_cast<f32x4*>(dst + d0) = f32x4{acc[db][qb][4 * g] * inv, acc[db][qb][4 * g + 1] * inv,
                                                       acc[db][qb][4 * g + 2] * inv, acc[db][qb][4 * g + 3] * inv};
         }
-      if (hf == 0 && cb == 0) lse[(int64_t(sp) * H + h) * sq + row] = (st.m_run[qb] + __log2f(lt)) * kLn2;
+      if (hf == 0) lse[(int64_t(sp) * H + h) * sq + row] = (st.m_run[qb] + __log2f(lt)) * kLn2;
     } else if (row < sq) {
-      uint16_t* dst = o + int64_t(row) * rowstride + int64_t(h) * D + cb * DV;
+      uint16_t* dst = o + int64_t(row) * rowstride + int64_t(h) * D;
 #pragma unroll
       for (int db = 0; db < G::kND; ++db)
 #pragma unroll
@@ -876,18 +863,18 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(const uint16_t* __r
           w[1] = pack_bf16x2(acc[db][qb][4 * g + 2] * inv, acc[db][qb][4 * g + 3] * inv);
           *reinterpret_cast<u32x2*>(dst + d0) = w;
         }
-      if (lse && hf == 0 && cb == 0) lse[int64_t(h) * sq + row] = (st.m_run[qb] + __log2f(lt)) * kLn2;
+      if (lse && hf == 0) lse[int64_t(h) * sq + row] = (st.m_run[qb] + __log2f(lt)) * kLn2;
     }
   }
 }
 
-template <int D, int DV, bool GV, bool SPLIT = false>
+template <int D, bool GV, bool SPLIT = false>
 hipError_t launch_d(const void* q, const KvArg<GV>& kv, void* o, float* lse, int64_t sq, int64_t skv, int H,
                     float c, hipStream_t stream, int nsplit = 1, float* opart = nullptr) {
-  const int64_t nqt = (sq + Geo<D, DV>::BM - 1) / Geo<D, DV>::BM;
-  const int64_t grid = nqt * H * (D / DV) * nsplit;  // the host has checked grid * kThreads <= kMaxItems
+  const int64_t nqt = (sq + Geo<D>::BM - 1) / Geo<D>::BM;
+  const int64_t grid = nqt * H * nsplit;  // the host has checked grid * kThreads <= kMaxItems
   if (grid > kMaxItems / kThreads) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((attn_bf16_kernel<D, DV, GV, SPLIT>), dim3(unsigned(grid)), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((attn_bf16_kernel<D, GV, SPLIT>), dim3(unsigned(grid)), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(q), kv, static_cast<uint16_t*>(o), lse, int(sq), int(skv), H, c,
                      int(nqt), nsplit, opart);
   return hipGetLastError();
@@ -925,16 +912,8 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ op
   if (lse && c4 == 0) lse[int64_t(h) * sq + row] = m + logf(ws);
 }
 
-template <int D, int DV>
-hipError_t launch_split(const void* q, const void* k, const void* v, void* o, float* lse, int64_t sq, int64_t skv,
-                        int H, float c, int nsplit, float* opart, float* lpart, hipStream_t stream) {
-  // Both grids are checked before the first launch, so a call that does not
-  // fit enqueues nothing.
-  if (attn_bf16_items(sq, H, D, nsplit) > kMaxItems || attn_merge_items(sq, H, D) > kMaxItems)
-    return hipErrorInvalidConfiguration;
-  const KvFlat kv{static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v)};
-  hipError_t e = launch_d<D, DV, false, true>(q, kv, o, lpart, sq, skv, H, c, stream, nsplit, opart);
-  if (e != hipSuccess) return e;
+hipError_t launch_merge(const float* opart, const float* lpart, void* o, float* lse, int nsplit, int64_t sq, int H,
+                        int D, hipStream_t stream) {
   const int64_t threads = sq * H * (D / 4);
   const int64_t blocks = (threads + 255) / 256;  // checked with the attention grid before either launch
   hipLaunchKernelGGL(merge_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, opart, lpart,
@@ -942,12 +921,25 @@ hipError_t launch_split(const void* q, const void* k, const void* v, void* o, fl
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_split(const void* q, const void* k, const void* v, void* o, float* lse, int64_t sq, int64_t skv,
+                        int H, float c, int nsplit, float* opart, float* lpart, hipStream_t stream) {
+  // Both grids are checked before the first launch, so a call that does not
+  // fit enqueues nothing.
+  if (attn_bf16_items(sq, H, D, nsplit) > kMaxItems || attn_merge_items(sq, H, D) > kMaxItems)
+    return hipErrorInvalidConfiguration;
+  const KvFlat kv{static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v)};
+  hipError_t e = launch_d<D, false, true>(q, kv, o, lpart, sq, skv, H, c, stream, nsplit, opart);
+  if (e != hipSuccess) return e;
+  return launch_merge(opart, lpart, o, lse, nsplit, sq, H, D, stream);
+}
+
 }  // namespace
 
 int64_t attn_bf16_items(int64_t sq, int H, int d, int nsplit) {
-  const int bm = d == 512 ? Geo<512, 256>::BM : Geo<128>::BM;
-  const int ncb = d == 512 ? 2 : 1;
-  const __int128 n = __int128((sq + bm - 1) / bm) * H * ncb * nsplit * kThreads;
+  if (d == 512) return attn_d512_items(sq, H, nsplit);
+  const int bm = Geo<128>::BM;
+  const __int128 n = __int128((sq + bm - 1) / bm) * H * nsplit * kThreads;
   return n > INT64_MAX ? INT64_MAX : int64_t(n);
 }
 
@@ -961,9 +953,9 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o
   if (sq > (int64_t(1) << 31) - 1024) return hipErrorInvalidValue;
   const float c = scale * 1.4426950408889634f;
   const KvFlat kv{static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v)};
-  if (d == 64) return launch_d<64, 64, false>(q, kv, o, lse, sq, skv, H, c, stream);
-  if (d == 512) return launch_d<512, 256, false>(q, kv, o, lse, sq, skv, H, c, stream);
-  return launch_d<128, 128, false>(q, kv, o, lse, sq, skv, H, c, stream);
+  if (d == 64) return launch_d<64, false>(q, kv, o, lse, sq, skv, H, c, stream);
+  if (d == 512) return launch_attn_d512(q, k, v, o, lse, sq, skv, H, c, 1, nullptr, stream);
+  return launch_d<128, false>(q, kv, o, lse, sq, skv, H, c, stream);
 }
 
 hipError_t launch_attn_bf16_gv(const void* q, const KvShards& kv, void* o, float* lse, int64_t sq, int H, int d,
@@ -971,8 +963,8 @@ hipError_t launch_attn_bf16_gv(const void* q, const KvShards& kv, void* o, float
   if (sq > (int64_t(1) << 31) - 1024) return hipErrorInvalidValue;
   const float c = scale * 1.4426950408889634f;
   const int64_t skv = kv.start[kv.W];
-  if (d == 64) return launch_d<64, 64, true>(q, kv, o, lse, sq, skv, H, c, stream);
-  return launch_d<128, 128, true>(q, kv, o, lse, sq, skv, H, c, stream);
+  if (d == 64) return launch_d<64, true>(q, kv, o, lse, sq, skv, H, c, stream);
+  return launch_d<128, true>(q, kv, o, lse, sq, skv, H, c, stream);
 }
 
 namespace {
@@ -1011,9 +1003,15 @@ hipError_t launch_attn_bf16_split(const void* q, const void* k, const void* v, v
                                   hipStream_t stream) {
   if (sq > (int64_t(1) << 31) - 1024) return hipErrorInvalidValue;
   const float c = scale * 1.4426950408889634f;
-  if (d == 64) return launch_split<64, 64>(q, k, v, o, lse, sq, skv, H, c, nsplit, opart, lpart, stream);
-  if (d == 512) return launch_split<512, 256>(q, k, v, o, lse, sq, skv, H, c, nsplit, opart, lpart, stream);
-  return launch_split<128, 128>(q, k, v, o, lse, sq, skv, H, c, nsplit, opart, lpart, stream);
+  if (d == 64) return launch_split<64>(q, k, v, o, lse, sq, skv, H, c, nsplit, opart, lpart, stream);
+  if (d == 512) {
+    if (attn_d512_items(sq, H, nsplit) > kMaxItems || attn_merge_items(sq, H, d) > kMaxItems)
+      return hipErrorInvalidConfiguration;
+    hipError_t e = launch_attn_d512(q, k, v, o, lpart, sq, skv, H, c, nsplit, opart, stream);
+    if (e != hipSuccess) return e;
+    return launch_merge(opart, lpart, o, lse, nsplit, sq, H, d, stream);
+  }
+  return launch_split<128>(q, k, v, o, lse, sq, skv, H, c, nsplit, opart, lpart, stream);
 }
 
 }  // namespace spattn

@@ -1,0 +1,443 @@
+// Attention at head size 512 (the VAE's single-head attention over C = 512
+// channels) with every score formed once.
+//
+// Page "NPU HunyuanImage-3.0模型推理优化实践", section VAE并行优化: each process
+// attends its block's queries to the keys and values of all blocks, one head
+// over all channels, scale 1/sqrt(C).  The plain definition is
+// O = softmax(Q K^T / sqrt(d)) V per head; this kernel computes it with an
+// online softmax over 32-key tiles.
+//
+// Why a kernel of its own.  At head size 512 a wave cannot hold both the Q
+// fragments of its 32 queries (128 registers) and the O accumulators of all
+// 512 output columns (256 registers) next to the scores, the operands in
+// flight and the softmax.  Instead, a work-group of 4 waves takes 128 queries:
+//   * wave w forms the scores S^T = K Q^T of query block w (32 queries) over
+//     the tile's 32 keys and their softmax, and writes the bf16 probabilities
+//     (already in the B-operand layout of the P*V MFMA) to LDS;
+//   * after a barrier, wave w accumulates output columns [128w, 128w + 128)
+//     for all four query blocks, reading P from LDS and V^T from the tile.
+// So every score is formed once, a lane holds 128 Q registers (VGPRs) and 256
+// accumulators (4 blocks x 4 column tiles x 16, all the AGPRs), and each K
+// operand read from LDS feeds one MFMA, each V^T operand four.  Per 32 keys
+// and 128 queries: 256 MFMAs of 32x32x16 against 160 KiB of LDS operand reads
+// and 64 KiB of tile writes.
+//
+// Softmax: float32, base 2 with the scale folded into log2(e).  The O
+// accumulators are never rescaled (as C++ on AGPR values, a rescale would make
+// the compiler keep VGPR copies of all 256 across the loop): each query's
+// reference is its first tile's maximum plus 40, so probabilities start at or
+// below 2^-40 (far above the underflow of any key within 86 of the maximum,
+// all that can matter) and may then grow to 2^64 before the float32 sums come
+// anywhere near overflow.  Only a score that tops its query's first-tile
+// maximum by more than 104 (log2 units, about 72 nats) needs a larger
+// reference: the work-group then restarts its keys with the raised reference.
+// Each restart is caused by a later tile than the previous one, so there are
+// at most as many restarts as tiles.
+//
+// K and V tiles stream through LDS with LDS-direct loads (no VGPR staging),
+// one tile ahead.  LDS rows are padded (K 1040 bytes, V 1088) rather than
+// swizzled, so every operand read is one per-lane base plus an immediate
+// offset; the padding spreads the rows that one read touches over the banks.
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace spattn {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int kD = 512;
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kBM = 32 * kWaves;            // query rows per work-group
+constexpr int kBN = 32;                     // keys per tile
+constexpr int kRowB = kD * 2;               // bytes per K / V row in global memory
+constexpr int kKS = kRowB + 16;             // LDS stride of a K row
+constexpr int kVS = kRowB + 64;             // LDS stride of a V row
+constexpr int kDC = kD / 16;                // k-steps of the score MFMA
+constexpr int kColsW = kD / kWaves;         // output columns per wave
+constexpr int kCT = kColsW / 32;            // 32-column O^T tiles per wave and query block
+constexpr int kRowsW = kBN / kWaves;        // tile rows each wave loads
+constexpr int kKRA = 4;                     // K operands read ahead of their MFMA
+constexpr float kOff = 40.0f;               // reference above a query's first-tile maximum (log2 units)
+constexpr float kCheck = 18446744073709551616.0f;  // 2^64: a lane's sum of 16 probabilities above it restarts
+constexpr float kLn2 = 0.69314718055994531f;
+
+// LDS: two K slots, two V slots, the probabilities of the four query blocks,
+// the restart flags of the current tile and the row sums (epilogue).
+constexpr int kKSlotB = kBN * kKS;
+constexpr int kVSlotB = kBN * kVS;
+constexpr int kOffK = 0;
+constexpr int kOffV = 2 * kKSlotB;
+constexpr int kOffP = kOffV + 2 * kVSlotB;             // [block][u][lane] 16 bytes
+constexpr int kOffF = kOffP + kWaves * 2 * 64 * 16;    // int flag[block]
+constexpr int kOffL = kOffF + 16;                      // float lsum[block][32]
+constexpr int kSmem = kOffL + kWaves * 32 * 4;
+static_assert(kSmem <= 160 * 1024, "LDS");
+
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  f32x2 f = {a, b};
+  bf16x2 h = __builtin_convertvector(f, bf16x2);  // v_cvt_pk_bf16_f32, nearest-even
+  return __builtin_bit_cast(uint32_t, h);
+}
+// v_permlane32_swap with both operands x returns, in some order that depends
+// on the wave half, the lane's own x and that of lane l ^ 32: the sum and the
+// maximum of the pair are the same in both halves.
+__device__ inline float halves_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
+__device__ inline float halves_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+}
+
+// s_waitcnt immediate: vmcnt(vm), expcnt untouched, lgkmcnt(0).
+constexpr unsigned waitcnt_vm_lgkm0(unsigned vm) { return (vm & 0xFu) | ((vm >> 4) << 14) | (0x7u << 4); }
+
+// This wave's older LDS-direct loads (all but the newest PENDING) have landed
+// and its LDS accesses have completed; then all waves meet.  The signal
+// fences keep the compiler from moving LDS accesses across.
+template <unsigned PENDING>
+__device__ inline void barrier_wait() {
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(PENDING));
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// One LDS-direct 16-byte load per lane: bytes [16 lane, 16 lane + 16) of the
+// global row at rsrc base + soffset into LDS row address m0 (both
+// wave-uniform).  Inline asm keeps the compiler from treating the in-flight
+// LDS writes as aliasing the LDS reads that follow; the kernel waits for them
+// itself (vmcnt) before the barrier that publishes a tile.
+__device__ inline void lds_load(const i32x4& rs, uint32_t m0, uint32_t soffset, uint32_t voffset) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(m0), "v"(voffset), "s"(rs), "s"(soffset)
+               : "memory", "m0");
+}
+
+// Buffer resource of a tile: base address, raw (stride 0), 2 GiB range.
+__device__ inline i32x4 rsrc(const char* base) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return i32x4{int(uint32_t(a)), int(uint32_t(a >> 32) & 0xFFFF), 0x7FFFFFFF, 0x00020000};
+}
+
+// Loads tile rows [8w, 8w + 8) of K and of V; rows past `valid` re-read row
+// valid-1 (finite data for keys that are masked to -inf).  Everything but the
+// lane's byte offset is wave-uniform.
+__device__ inline void load_tile(const char* kt, const char* vt, int valid, uint32_t rowbytes, uint32_t kslot,
+                                 uint32_t vslot, int wave, uint32_t lane16) {
+  const i32x4 rk = rsrc(kt), rv = rsrc(vt);
+#pragma unroll
+  for (int j = 0; j < kRowsW; ++j) {
+    const int r = wave * kRowsW + j;
+    const uint32_t so = uint32_t(r < valid ? r : valid - 1) * rowbytes;
+    lds_load(rk, kslot + r * kKS, so, lane16);
+    lds_load(rv, vslot + r * kVS, so, lane16);
+  }
+}
+
+// Probabilities of the wave's 32 x 32 score block under reference m (per
+// query column, log2 units): w[u][e] packs scores r = 8u + 2e, 8u + 2e + 1 of
+// the lane's accumulator (B operand of P*V MFMA u); returns the lane's sum of
+// the 16 bf16 probabilities.
+__device__ inline float make_words(const f32x16& s, float c, float m, uint32_t (&w)[2][4]) {
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float ls = 0.f;
+#pragma unroll
+  for (int pr = 0; pr < 8; ++pr) {
+    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[2 * pr], c, -m));
+    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[2 * pr + 1], c, -m));
+    const uint32_t word = pack_bf16x2(p0, p1);
+    w[pr >> 2][pr & 3] = word;
+    ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, word), ones, ls, false);
+  }
+  return ls;
+}
+
+// Score MFMAs.  The O accumulators take all 256 AGPRs (the P*V MFMAs are
+// compiler builtins in AGPR form), so the scores must stay in VGPRs: these
+// three are written as inline asm with VGPR operands.  The compiler's hazard
+// checks do not see inside them, so they carry their own: the chain's first
+// MFMA starts from the inline constant 0 (no register written by another
+// unit), dependent MFMAs of one chain may issue back to back, and the last is
+// followed by 16 wait states before anything can read its result (a 32x32x16
+// bf16 MFMA needs 12 before a VALU read).
+__device__ inline f32x16 mfma_s_first(const bf16x8& a, const bf16x8& b) {
+  f32x16 d;
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+  return d;
+}
+__device__ inline void mfma_s(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ inline void mfma_s_last(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7" : "+v"(d) : "v"(a), "v"(b));
+}
+
+// Maximum of the block per query column (both wave halves), in log2 units.
+__device__ inline float col_max(const f32x16& s, float c) {
+  float m = s[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) m = fmaxf(m, s[r]);
+  return halves_max(m) * c;
+}
+
+// SPLIT: the keys are cut into nsplit ranges of whole tiles; work-group
+// (range, query tile, head) writes its float32 O normalised over its own keys
+// (opart [nsplit, sq, H, 512]) and that range's LSE (lse [nsplit, H, sq]).
+// Ranges vary fastest over the work-groups, so with 8 ranges the work-groups
+// of one range share an XCD (and its L2) when blocks are dealt round-robin.
+template <bool SPLIT>
+__global__ __launch_bounds__(kThreads) void attn_d512_kernel(const uint16_t* __restrict__ q,
+                                                             const uint16_t* __restrict__ k,
+                                                             const uint16_t* __restrict__ v,
+                                                             uint16_t* __restrict__ o, float* __restrict__ lse,
+                                                             int sq, int skv_all, int H, float c, int nqt,
+                                                             int nsplit, float* __restrict__ opart) {
+  __shared__ __attribute__((aligned(1024))) char smem[kSmem];
+  const uint32_t sbase = uint32_t(reinterpret_cast<uintptr_t>(smem));
+
+  const int L = blockIdx.x;
+  int qt, h, sp = 0;
+  if constexpr (SPLIT) {
+    sp = L % nsplit;
+    const int rest = L / nsplit;
+    qt = rest % nqt;
+    h = rest / nqt;
+  } else {
+    h = L / nqt;
+    qt = L - h * nqt;
+  }
+  int k0 = 0, skv = skv_all;
+  if constexpr (SPLIT) {
+    const int tiles = (skv_all + kBN - 1) / kBN;
+    k0 = int(int64_t(tiles) * sp / nsplit) * kBN;
+    skv = min(skv_all, int(int64_t(tiles) * (sp + 1) / nsplit) * kBN) - k0;
+  }
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31;
+  const int hf = lane >> 5;
+  const int64_t rowstride = int64_t(H) * kD;
+  const uint32_t rowbytes = uint32_t(rowstride * 2);  // the host keeps 32 rows below 2 GiB
+  const char* kh = reinterpret_cast<const char*>(k + int64_t(k0) * rowstride + int64_t(h) * kD);
+  const char* vh = reinterpret_cast<const char*>(v + int64_t(k0) * rowstride + int64_t(h) * kD);
+  const int nT = (skv + kBN - 1) / kBN;
+  const int64_t tb = int64_t(kBN) * rowbytes;
+  const uint32_t lane16 = uint32_t(lane) * 16;
+
+  auto kslot = [&](int j) { return sbase + kOffK + (unsigned(j) & 1u) * kKSlotB; };
+  auto vslot = [&](int j) { return sbase + kOffV + (unsigned(j) & 1u) * kVSlotB; };
+  load_tile(kh, vh, min(skv, kBN), rowbytes, kslot(0), vslot(0), wave, lane16);
+
+  // Q fragments of this wave's query block (B operand of S^T = K Q^T): lane
+  // holds 8 channels of query `col` per k-step.  Rows past sq repeat row
+  // sq-1: their columns are computed and never written.
+  bf16x8 qf[kDC];
+  {
+    const int row = min(qt * kBM + wave * 32 + col, sq - 1);
+    const u32x4* src = reinterpret_cast<const u32x4*>(q + int64_t(row) * rowstride + int64_t(h) * kD + 8 * hf);
+#pragma unroll
+    for (int cc = 0; cc < kDC; ++cc) qf[cc] = __builtin_bit_cast(bf16x8, src[2 * cc]);
+  }
+
+  // O^T accumulators: [query block][column tile of this wave].  Every value
+  // they take is an MFMA result (zero included), so they stay in AGPRs.
+  const bf16x8 zb = {};
+  f32x16 acc[kWaves][kCT];
+#pragma unroll
+  for (int b = 0; b < kWaves; ++b)
+#pragma unroll
+    for (int ct = 0; ct < kCT; ++ct) acc[b][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zb, zb, f32x16{}, 0, 0, 0);
+  float m_run = -INFINITY;  // this wave's query block: reference (log2 units), the same in both halves
+  float l_run = 0.f;        // the lane's partial row sum
+
+  const char* lds = reinterpret_cast<const char*>(smem);
+  // Per-lane operand bases: K row `col`, chunk hf (+32 bytes per k-step);
+  // V^T rows 4hf + j16/4 (+16 rows per MFMA u, +8 for the second half) and
+  // channels 128w + 16(g16 & 1) + 4(j16 & 3) (+32 per column tile).
+  const int g16 = lane >> 4, j16 = lane & 15;
+  const uint32_t koff = uint32_t(col * kKS + hf * 16);
+  const uint32_t voff = uint32_t((4 * hf + (j16 >> 2)) * kVS + (wave * kColsW + 16 * (g16 & 1) + 4 * (j16 & 3)) * 2);
+
+  for (int t = 0; t < nT; ++t) {
+    barrier_wait<0>();  // tile t has landed; every wave is done with tile t-1
+    if (t + 1 < nT)
+      load_tile(kh + (t + 1) * tb, vh + (t + 1) * tb, min(skv - (t + 1) * kBN, kBN), rowbytes, kslot(t + 1),
+                vslot(t + 1), wave, lane16);
+    const char* kb = lds + (kslot(t) - sbase) + koff;
+    const char* vb = lds + (vslot(t) - sbase) + voff;
+
+    // ---- scores of this wave's query block over the tile's 32 keys; the K
+    // operands are read kKRA MFMAs ahead, each read-MFMA pair fenced in order
+    f32x16 s;
+    {
+      auto kread = [&](int cc) { return *reinterpret_cast<const bf16x8*>(kb + 32 * cc); };
+      bf16x8 kf[kKRA];
+#pragma unroll
+      for (int i = 0; i < kKRA; ++i) kf[i] = kread(i);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int cc = 0; cc < kDC; ++cc) {
+        const bf16x8 a = kf[cc % kKRA];
+        if (cc + kKRA < kDC) kf[cc % kKRA] = kread(cc + kKRA);
+        if (cc == 0) s = mfma_s_first(a, qf[0]);
+        else if (cc + 1 < kDC) mfma_s(s, a, qf[cc]);
+        else mfma_s_last(s, a, qf[cc]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const int key_last = skv - t * kBN;  // keys at or past this index are masked
+      if (key_last < kBN) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (8 * (r >> 2) + 4 * hf + (r & 3) >= key_last) s[r] = -INFINITY;
+      }
+    }
+
+    // ---- softmax of the block; probabilities to LDS for every wave
+    uint32_t w[2][4];
+    if (t == 0) m_run = fmaxf(m_run, col_max(s, c) + kOff);  // every column has a key in the first tile
+    const float ls = make_words(s, c, m_run, w);
+    const bool over = __builtin_amdgcn_ballot_w64(ls > kCheck) != 0;
+    if (over) m_run = fmaxf(m_run, col_max(s, c) + kOff);
+    l_run += ls;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      *reinterpret_cast<u32x4*>(smem + kOffP + ((wave * 2 + u) * 64 + lane) * 16) =
+          u32x4{w[u][0], w[u][1], w[u][2], w[u][3]};
+    if (lane == 0) *reinterpret_cast<int*>(smem + kOffF + wave * 4) = over ? 1 : 0;
+    barrier_wait<63>();  // probabilities and flags visible; the next tile's loads stay in flight
+
+    // ---- restart (rare): some query's reference was raised; every wave
+    // starts over from the first tile (the raised references carry over)
+    {
+      const i32x4 fl = *reinterpret_cast<const i32x4*>(smem + kOffF);
+      if (__builtin_amdgcn_readfirstlane(fl[0] | fl[1] | fl[2] | fl[3]) != 0) {
+#pragma unroll
+        for (int b = 0; b < kWaves; ++b)
+#pragma unroll
+          for (int ct = 0; ct < kCT; ++ct)
+            acc[b][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zb, zb, f32x16{}, 0, 0, 0);
+        l_run = 0.f;
+        barrier_wait<0>();  // the next tile's loads have landed and every wave has read the flags
+        load_tile(kh, vh, min(skv, kBN), rowbytes, kslot(0), vslot(0), wave, lane16);
+        t = -1;
+        continue;
+      }
+    }
+
+    // ---- O^T[cols of this wave][queries of block b] += V^T P^T over the tile
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      auto pread = [&](int b, int u) {
+        return *reinterpret_cast<const bf16x8*>(smem + kOffP + ((b * 2 + u) * 64 + lane) * 16);
+      };
+      // V^T operand of MFMA u, column tile ct: channels [32 ct, 32 ct + 32) of
+      // this wave x the 16 keys of u, in the key order of the probability words.
+      auto vread = [&](int u, int ct) {
+        const char* p0 = vb + u * 16 * kVS + ct * 64;
+        const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
+        const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 8 * kVS));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        bf16x8 pf[kWaves];
+#pragma unroll
+        for (int b = 0; b < kWaves; ++b) pf[b] = pread(b, u);
+        bf16x8 vf = vread(u, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ct = 0; ct < kCT; ++ct) {
+          const bf16x8 vc = vf;
+          if (ct + 1 < kCT) vf = vread(u, ct + 1);
+#pragma unroll
+          for (int b = 0; b < kWaves; ++b)
+            acc[b][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vc, pf[b], acc[b][ct], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+  }
+
+  // ---- epilogue: row sums of every block through LDS, O = O^T / l
+  const float l_tot = halves_sum(l_run);
+  if (hf == 0) *reinterpret_cast<float*>(smem + kOffL + (wave * 32 + col) * 4) = l_tot;
+  {
+    const int row = qt * kBM + wave * 32 + col;
+    if (hf == 0 && row < sq) {
+      const float lv = (m_run + __log2f(l_tot)) * kLn2;
+      if (SPLIT) lse[(int64_t(sp) * H + h) * sq + row] = lv;
+      else if (lse) lse[int64_t(h) * sq + row] = lv;
+    }
+  }
+  barrier_wait<0>();
+#pragma unroll
+  for (int b = 0; b < kWaves; ++b) {
+    const int row = qt * kBM + b * 32 + col;
+    const float inv = 1.f / *reinterpret_cast<const float*>(smem + kOffL + (b * 32 + col) * 4);
+    if (row >= sq) continue;
+#pragma unroll
+    for (int ct = 0; ct < kCT; ++ct) {
+      const int cb = wave * kColsW + ct * 32;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = cb + 8 * g + 4 * hf;
+        const f32x16& a = acc[b][ct];
+        if (SPLIT) {
+          float* dst = opart + (int64_t(sp) * sq + row) * rowstride + int64_t(h) * kD + d0;
+          *reinterpret_cast<f32x4*>(dst) =
+              f32x4{a[4 * g] * inv, a[4 * g + 1] * inv, a[4 * g + 2] * inv, a[4 * g + 3] * inv};
+        } else {
+          uint16_t* dst = o + int64_t(row) * rowstride + int64_t(h) * kD + d0;
+          *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(a[4 * g] * inv, a[4 * g + 1] * inv),
+                                                 pack_bf16x2(a[4 * g + 2] * inv, a[4 * g + 3] * inv)};
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+int64_t attn_d512_items(int64_t sq, int H, int nsplit) {
+  const __int128 n = __int128((sq + kBM - 1) / kBM) * H * nsplit * kThreads;
+  return n > INT64_MAX ? INT64_MAX : int64_t(n);
+}
+
+hipError_t launch_attn_d512(const void* q, const void* k, const void* v, void* o, float* lse, int64_t sq,
+                            int64_t skv, int H, float c, int nsplit, float* opart, hipStream_t stream) {
+  if (sq < 1) return hipSuccess;
+  if (int64_t(H) * kRowB * kBN >= (int64_t(1) << 31)) return hipErrorInvalidValue;  // 32-bit row offsets
+  const int64_t nqt = (sq + kBM - 1) / kBM;
+  const int64_t grid = nqt * H * nsplit;  // the host has checked grid * kThreads <= kMaxItems
+  if (grid > kMaxItems / kThreads) return hipErrorInvalidConfiguration;
+  if (opart)
+    hipLaunchKernelGGL(attn_d512_kernel<true>, dim3(unsigned(grid)), dim3(kThreads), 0, stream,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                       static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, int(sq), int(skv), H, c,
+                       int(nqt), nsplit, opart);
+  else
+    hipLaunchKernelGGL(attn_d512_kernel<false>, dim3(unsigned(grid)), dim3(kThreads), 0, stream,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                       static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, int(sq), int(skv), H, c,
+                       int(nqt), 1, opart);
+  return hipGetLastError();
+}
+
+}  // namespace spattn

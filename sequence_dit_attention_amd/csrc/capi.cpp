@@ -339,15 +339,19 @@ int sp_tile_bounds(int64_t Hh, int64_t Ww, int32_t pr, int32_t pc, int32_t p, in
 
 namespace {
 
-// Copies between a channels-last raster [Hh, Ww, C] and its pr*pc blocks laid
-// out one after another in block order (each block row-major).  One segment
-// per block with one outer step per pixel row of the block, all blocks in one
-// batch of copies.
-int tile_copy(const char* fn, bool to_flat, int32_t dtype, const void* raster, void* raster_out, int64_t Hh,
-              int64_t Ww, int64_t C, int32_t pr, int32_t pc, const void* flat_in, void* flat_out,
-              int64_t flat_elems, void* stream) {
+// Copies between channels-last rasters [Hh, Ww, C] and their pr*pc blocks
+// laid out one after another in block order (each block row-major), for n
+// (raster, flat) pairs of one shape.  One segment per (pair, block) with one
+// outer step per pixel row of the block, all in one batch of copies.
+constexpr int32_t kMaxTilePairs = 16;
+
+int tile_copy(const char* fn, bool to_flat, int32_t dtype, int32_t npair, const void* const* rasters, int64_t Hh,
+              int64_t Ww, int64_t C, int32_t pr, int32_t pc, const void* const* flats, int64_t flat_elems,
+              void* stream) {
   const int eb = elem_bytes(dtype);
   if (!eb) return fail(SP_EINVAL, "%s: unknown dtype %d", fn, dtype);
+  if (npair < 1 || npair > kMaxTilePairs) return fail(SP_EINVAL, "%s: need 1 <= n <= %d", fn, kMaxTilePairs);
+  if (!rasters || !flats) return fail(SP_EINVAL, "%s: null pointer table", fn);
   if (pr < 1 || pc < 1 || int64_t(pr) * pc > 65536) return fail(SP_EINVAL, "%s: need 1 <= pr*pc <= 65536", fn);
   if (Hh < 0 || Ww < 0 || C < 0 || flat_elems < 0) return fail(SP_EINVAL, "%s: negative size", fn);
   int64_t n, bytes;
@@ -356,27 +360,37 @@ int tile_copy(const char* fn, bool to_flat, int32_t dtype, const void* raster, v
   if (flat_elems < n) return fail(SP_ERANGE, "%s: flat holds %lld elements, the blocks need %lld", fn,
                                   (long long)flat_elems, (long long)n);
   if (n == 0) return ok();
-  const void* rp = to_flat ? raster : raster_out;
-  const void* fp = to_flat ? static_cast<const void*>(flat_out) : flat_in;
-  if (!rp || !fp) return fail(SP_EINVAL, "%s: null device pointer", fn);
-  if (ranges_overlap(rp, bytes, fp, bytes)) return fail(SP_EOVERLAP, "%s: raster and flat overlap", fn);
-  const int64_t rowpitch = Ww * C * eb;  // bytes per raster row
-  std::vector<CopySeg> segs;
-  int64_t off = 0;  // element offset of the current block in flat
-  for (int32_t i = 0; i < pr; ++i) {
-    const __int128 h = Hh, w = Ww;
-    const int64_t r0 = static_cast<int64_t>((h * i) / pr), r1 = static_cast<int64_t>((h * (i + 1)) / pr);
-    for (int32_t j = 0; j < pc; ++j) {
-      const int64_t c0 = static_cast<int64_t>((w * j) / pc), c1 = static_cast<int64_t>((w * (j + 1)) / pc);
-      const int64_t bw = (c1 - c0) * C * eb;  // bytes per block row
-      char* fl = static_cast<char*>(const_cast<void*>(fp)) + off * eb;
-      char* ra = static_cast<char*>(const_cast<void*>(rp)) + r0 * rowpitch + c0 * C * eb;
-      if (to_flat) segs.push_back(CopySeg{ra, fl, bw, rowpitch, bw, r1 - r0});
-      else segs.push_back(CopySeg{fl, ra, bw, bw, rowpitch, r1 - r0});
-      off += (r1 - r0) * (c1 - c0) * C;
+  for (int32_t a = 0; a < npair; ++a) {
+    if (!rasters[a] || !flats[a]) return fail(SP_EINVAL, "%s: null device pointer", fn);
+    // The written buffers (flats when packing, rasters when unpacking) must
+    // not overlap any buffer of the call.
+    const void* wa = to_flat ? flats[a] : rasters[a];
+    for (int32_t b = 0; b < npair; ++b) {
+      if (ranges_overlap(wa, bytes, to_flat ? rasters[b] : flats[b], bytes))
+        return fail(SP_EOVERLAP, "%s: raster and flat overlap", fn);
+      if (b != a && ranges_overlap(wa, bytes, to_flat ? flats[b] : rasters[b], bytes))
+        return fail(SP_EOVERLAP, "%s: two output buffers overlap", fn);
     }
   }
-  // one segment per block, each with its own number of pixel rows
+  const int64_t rowpitch = Ww * C * eb;  // bytes per raster row
+  std::vector<CopySeg> segs;
+  for (int32_t a = 0; a < npair; ++a) {
+    int64_t off = 0;  // element offset of the current block in flat
+    for (int32_t i = 0; i < pr; ++i) {
+      const __int128 h = Hh, w = Ww;
+      const int64_t r0 = static_cast<int64_t>((h * i) / pr), r1 = static_cast<int64_t>((h * (i + 1)) / pr);
+      for (int32_t j = 0; j < pc; ++j) {
+        const int64_t c0 = static_cast<int64_t>((w * j) / pc), c1 = static_cast<int64_t>((w * (j + 1)) / pc);
+        const int64_t bw = (c1 - c0) * C * eb;  // bytes per block row
+        char* fl = static_cast<char*>(const_cast<void*>(flats[a])) + off * eb;
+        char* ra = static_cast<char*>(const_cast<void*>(rasters[a])) + r0 * rowpitch + c0 * C * eb;
+        if (to_flat) segs.push_back(CopySeg{ra, fl, bw, rowpitch, bw, r1 - r0});
+        else segs.push_back(CopySeg{fl, ra, bw, bw, rowpitch, r1 - r0});
+        off += (r1 - r0) * (c1 - c0) * C;
+      }
+    }
+  }
+  // one segment per (pair, block), each with its own number of pixel rows
   return launch_copies(segs, 0, stream);
 }
 
@@ -384,13 +398,20 @@ int tile_copy(const char* fn, bool to_flat, int32_t dtype, const void* raster, v
 
 int tile_pack(int32_t dtype, const void* raster, int64_t Hh, int64_t Ww, int64_t C, int32_t pr, int32_t pc,
               void* flat, int64_t flat_elems, void* stream) {
-  return tile_copy("tile_pack", true, dtype, raster, nullptr, Hh, Ww, C, pr, pc, nullptr, flat, flat_elems, stream);
+  const void* fl = flat;
+  return tile_copy("tile_pack", true, dtype, 1, &raster, Hh, Ww, C, pr, pc, &fl, flat_elems, stream);
+}
+
+int tile_pack_n(int32_t dtype, int32_t n, const void* const* rasters, int64_t Hh, int64_t Ww, int64_t C, int32_t pr,
+                int32_t pc, void* const* flats, int64_t flat_elems, void* stream) {
+  return tile_copy("tile_pack_n", true, dtype, n, rasters, Hh, Ww, C, pr, pc,
+                   const_cast<const void* const*>(flats), flat_elems, stream);
 }
 
 int tile_unpack(int32_t dtype, const void* flat, int64_t flat_elems, int64_t Hh, int64_t Ww, int64_t C, int32_t pr,
                 int32_t pc, void* raster, void* stream) {
-  return tile_copy("tile_unpack", false, dtype, nullptr, raster, Hh, Ww, C, pr, pc, flat, nullptr, flat_elems,
-                   stream);
+  const void* ra = raster;
+  return tile_copy("tile_unpack", false, dtype, 1, &ra, Hh, Ww, C, pr, pc, &flat, flat_elems, stream);
 }
 
 int qk_norm_rope(int32_t dtype, const void* x, void* y, int64_t s, int32_t H, int32_t d, const float* gamma,

@@ -70,6 +70,15 @@ hipError_t launch_attn_bf16_gv(const void* q, const KvShards& kv, void* o, float
 hipError_t launch_attn_f32_gv(const float* q, const KvShards& kv, float* o, float* lse, int64_t sq, int H, int d,
                               float scale, hipStream_t stream);
 
+// Head size 512 (bf16, its own kernel: every score formed once).  c is the
+// softmax scale times log2(e).  opart == nullptr: writes o and lse (may be
+// null); otherwise the keys are cut into nsplit ranges and the call writes
+// float32 partials opart [nsplit, sq, H, 512] and their LSE into lse
+// ([nsplit, H, sq]) for the merge of launch_attn_bf16_split.
+hipError_t launch_attn_d512(const void* q, const void* k, const void* v, void* o, float* lse, int64_t sq,
+                            int64_t skv, int H, float c, int nsplit, float* opart, hipStream_t stream);
+int64_t attn_d512_items(int64_t sq, int H, int nsplit);
+
 // Device scratch of the split attention's allocation-free entry point: one
 // file-scope array per device (kScratchBytes, 256-byte aligned), held until
 // the process ends.  scratch_address() gives the current device's copy; the

@@ -117,8 +117,9 @@ class VaeBlockShare:
     map is cut along height and width into pr x pc blocks, one per process;
     attention gathers the K and V of all blocks; the outputs are gathered back
     in two stages and put at their spatial positions.  Per step:
-      1. gather of the K and V blocks in process order (tile_pack of the
-         channels-last rasters: the AllGatherV receive buffers),
+      1. gather of the K and V blocks in process order (tile_pack_n of the
+         two channels-last rasters, one batch of copies: the AllGatherV
+         receive buffers),
       2. attention of process p's block queries against all gathered keys,
          one head over the C channels, keys cut into nsplit ranges,
          written straight into p's slot of the flat output,
@@ -157,8 +158,7 @@ class VaeBlockShare:
         self.q_block.copy_(flat[self.off:self.off + self.m])
 
     def gather_kv(self) -> None:
-        api.tile_pack(self.k, self.pr, self.pc, self.k_flat)
-        api.tile_pack(self.v, self.pr, self.pc, self.v_flat)
+        api.tile_pack_n([self.k, self.v], self.pr, self.pc, [self.k_flat, self.v_flat])
 
     def attend(self) -> None:
         C = self.C
@@ -174,6 +174,25 @@ class VaeBlockShare:
         self.gather_kv()
         self.attend()
         self.place_out()
+
+    def capture(self) -> torch.cuda.CUDAGraph:
+        """The step recorded as a HIP graph.  The share is four short launches
+        around one attention launch, so issuing it from the host leaves the
+        GPU idle between them; a replay issues all of them at once.  Nothing in
+        the step allocates, synchronises or clears memory.  Each replay reads
+        whatever the input rasters hold at that time (their addresses are
+        recorded, so the rasters and this object must stay alive)."""
+        if self.k is None:
+            raise RuntimeError("set_inputs first")
+        side = torch.cuda.Stream(device=self.k.device)  # default priority
+        side.wait_stream(torch.cuda.current_stream(self.k.device))
+        with torch.cuda.stream(side):
+            self.step()  # first use of every launch outside the capture
+        torch.cuda.current_stream(self.k.device).wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.step()
+        return g
 
     def attn_flops(self) -> int:
         return 4 * self.m * self.n * self.C

@@ -28,7 +28,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert "shard_attn_fwd" in names and "shard_attn_fwd_gv" in names and len(names) == 19
+    assert "shard_attn_fwd" in names and "shard_attn_fwd_gv" in names and len(names) == 20
     h = ctypes.CDLL(_lib.LIB_PATH)
     for n in names:
         assert hasattr(h, n), n
@@ -205,6 +205,26 @@ def test_tile_bounds_match_oracle_and_validation():
     assert g(1, FAKE * 2, 128, 4, 4, 8, 2, 2, None, None) == SP_EINVAL      # null raster
     assert g(1, FAKE * 2, 100, 4, 4, 8, 2, 2, FAKE, None) == SP_ERANGE
     assert g(1, FAKE * 2, 0, 0, 4, 8, 2, 2, None, None) == 0                # nothing to do
+
+
+def test_tile_pack_n_validation():
+    """The multi-tensor block gather checks every pair (and the pairs against each
+    other) before anything is enqueued; 4 x 4 x 8 bf16 rasters are 256 bytes."""
+    L = _lib.lib()
+    P = ctypes.c_void_p
+    tab = lambda *a: (P * len(a))(*a)
+    f = L.tile_pack_n
+    R = tab(FAKE, FAKE * 3)
+    assert f(1, 0, R, 4, 4, 8, 2, 2, tab(FAKE * 2), 128, None) == SP_EINVAL           # n = 0
+    assert f(1, 17, R, 4, 4, 8, 2, 2, R, 128, None) == SP_EINVAL                       # n > 16
+    assert f(1, 2, None, 4, 4, 8, 2, 2, tab(FAKE * 2, FAKE * 4), 128, None) == SP_EINVAL  # null table
+    assert f(1, 2, R, 4, 4, 8, 2, 2, tab(FAKE * 2, None), 128, None) == SP_EINVAL      # null flat
+    assert f(1, 2, R, 4, 4, 8, 2, 2, tab(FAKE * 2, FAKE * 4), 127, None) == SP_ERANGE  # flats too small
+    assert f(1, 2, R, 4, 4, 8, 2, 2, tab(FAKE * 2, FAKE * 3 + 64), 128, None) == SP_EOVERLAP  # flat on a raster
+    assert f(1, 2, R, 4, 4, 8, 2, 2, tab(FAKE * 3 + 256, FAKE), 128, None) == SP_EOVERLAP     # flat 1 on raster 0
+    assert f(1, 2, R, 4, 4, 8, 2, 2, tab(FAKE * 2, FAKE * 2 + 128), 128, None) == SP_EOVERLAP  # flats overlap
+    assert f(7, 2, R, 4, 4, 8, 2, 2, tab(FAKE * 2, FAKE * 4), 128, None) == SP_EINVAL  # dtype
+    assert f(1, 2, R, 0, 4, 8, 2, 2, tab(FAKE * 2, FAKE * 4), 0, None) == 0            # nothing to do
 
 
 def test_split_attention_validation():

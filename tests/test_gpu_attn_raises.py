@@ -82,3 +82,41 @@ def test_reference_raises_split(d):
     o = sp.shard_attn_fwd_split(q, k, v, nsplit=3, lse=lse)
     torch.cuda.synchronize()
     _check(o, lse, qb, kb, vb)
+
+
+def _restart_inputs(sq, skv, d, seed, positions):
+    """Spikes that climb by about 120 (base 2) from one spike of an axis to the next:
+    more than the head-size-512 kernel absorbs without a larger reference."""
+    rng = np.random.default_rng(seed)
+    q = 0.5 * rng.standard_normal((sq, 1, d))
+    k = 0.5 * rng.standard_normal((skv, 1, d))
+    v = rng.standard_normal((skv, 1, d))
+    q[0::2, :, 0] += 4.0
+    q[1::2, :, 1] += 4.0
+    step = 120.0 * np.sqrt(d) / (4.0 * np.log2(np.e))
+    for i, p in enumerate(positions):
+        k[p, :, i % 2] += 4.0 + step * (i // 2)
+    return [f32_to_bf16_bits(a.astype(np.float32)) for a in (q, k, v)]
+
+
+@pytest.mark.parametrize("nsplit", [1, 2, 3])
+def test_d512_restarts_on_large_score_jumps(nsplit):
+    """Head size 512 keeps its accumulators unscaled and restarts the key loop when a
+    score tops its query's first-tile maximum by more than 104 (base 2).  Spikes
+    climbing ~120 per step force several restarts per work-group: at a tile's first
+    key, at a tile edge, deep in the keys, in the ragged last tile and on the last
+    key (two axes, so neighbouring query blocks restart at different tiles); with
+    key ranges, some ranges restart and others do not.  Checked against the float64
+    oracle (output dominated by the last spike of the row's axis) and its LSE."""
+    sq, skv, d = 293, 1000, 512
+    pos = [0, 1, 40, 63, 100, 300, 700, 990, 999]
+    qb, kb, vb = _restart_inputs(sq, skv, d, 11 + nsplit, pos)
+    q, k, v = (to_dev(a, "bf16") for a in (qb, kb, vb))
+    lse = torch.empty(1, sq, dtype=torch.float32, device="cuda")
+    if nsplit == 1:
+        o = sp.shard_attn_fwd(q, k, v, lse=lse)
+    else:
+        o = sp.shard_attn_fwd_split(q, k, v, nsplit=nsplit, lse=lse)
+    torch.cuda.synchronize()
+    assert np.isfinite(to_f64(o)).all()
+    _check(o, lse, qb, kb, vb)

@@ -44,3 +44,35 @@ def test_unpack_leaves_a_larger_flat_tail_alone_and_writes_every_raster_element(
     sp.tile_unpack(flat, Hh, Ww, pr, pc, raster)
     torch.cuda.synchronize()
     assert np.array_equal(raster.cpu().numpy(), oracle.tile_unpack(vals, Hh, Ww, pr, pc))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("Hh,Ww,C,pr,pc,n", [(7, 5, 3, 2, 3, 2), (128, 128, 512, 2, 2, 2), (84, 48, 512, 3, 3, 3),
+                                            (3, 2, 8, 3, 20, 2), (40, 40, 6, 6, 7, 5), (9, 1, 2, 2, 4, 16)])
+def test_tile_pack_n_bitwise_into_guarded_flats(dtype, Hh, Ww, C, pr, pc, n):
+    """Several rasters in one batch of copies (the K and V gathers of the VAE split): each
+    flat equals the oracle's block gather of its raster bit for bit, and the bytes
+    around every flat (one buffer holding all of them with gaps) stay untouched.
+    Grids with more than 32 segments in total span several launches."""
+    rng = np.random.default_rng(Hh * 7 + Ww * 3 + n)
+    rasters = []
+    for _ in range(n):
+        bits = rng.integers(0, 0x7F00, size=(Hh, Ww, C), dtype=np.uint16) if dtype == "bf16" else \
+            rng.standard_normal((Hh, Ww, C)).astype(np.float32)
+        rasters.append(bits)
+    dev = [to_dev(b, dtype) for b in rasters]
+    m = Hh * Ww * C
+    gap = 256  # elements between flats (and before the first / after the last)
+    tdt = dev[0].dtype
+    sent = -7.0
+    buf = torch.full((gap + n * (m + gap),), sent, dtype=tdt, device="cuda")
+    flats = [buf[gap + a * (m + gap): gap + a * (m + gap) + m].view(Hh * Ww, C) for a in range(n)]
+    sp.tile_pack_n(dev, pr, pc, flats)
+    torch.cuda.synchronize()
+    for a in range(n):
+        want = oracle.tile_pack(rasters[a], pr, pc)
+        assert to_host_bits(flats[a]).tobytes() == np.ascontiguousarray(want).tobytes(), a
+    host = buf.float().cpu().numpy()
+    for a in range(n + 1):
+        g0 = a * (m + gap)
+        assert np.all(host[g0:g0 + gap] == sent), a
