@@ -27,8 +27,8 @@ sys.path.insert(0, ROOT)
 METRIC = "shard-attention TFLOP/s (% bf16 MFMA peak) + varlen pack GB/s (% HBM), 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
-ATTN_SRC = os.path.join(ROOT, "sequence_dit_attention_amd", "csrc", "attn_bf16.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_traffic.json")
+ATTN_SRC = os.path.join(ROOT, "sequence_dit_attention_amd", "csrc", "attn_d128.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_d128_traffic.json")
 
 
 def log(msg: str) -> None:

@@ -31,13 +31,15 @@ COMMON = [
 ]
 
 
-# Per-file flags.  The head-size 64/128 attention kernel keeps every MFMA
-# operand and result in VGPRs (the scores feed VALU softmax code; AGPR copies
-# would cost more than they save); the head-size-512 kernel keeps its O
-# accumulators in AGPRs (the default MFMA form; its score MFMAs are inline asm
-# on VGPRs).  Neither needs NaN canonicalisation before its max reductions.
+# Per-file flags.  The head-size-64 attention kernel keeps every MFMA operand
+# and result in VGPRs (the scores feed VALU softmax code; AGPR copies would
+# cost more than they save); the head-size-128 kernel writes all its MFMAs as
+# inline asm on VGPRs; the head-size-512 kernel keeps its O accumulators in
+# AGPRs (the default MFMA form; its score MFMAs are inline asm on VGPRs).  None
+# needs NaN canonicalisation before its max reductions.
 EXTRA = {
     "attn_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true", "-fno-honor-nans"],
+    "attn_d128.hip": ["-fno-honor-nans"],
     "attn_d512.hip": ["-fno-honor-nans"],
 }
 

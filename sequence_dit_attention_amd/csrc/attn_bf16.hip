@@ -1,4 +1,7 @@
-// bf16 flash attention of a rank's local queries against the full K/V, gfx950.
+// bf16 flash attention of a rank's local queries against the full K/V, gfx950:
+// the kernel for head size 64, the merge of split-key partials, and the
+// dispatch by head size (128 and 512 have kernels of their own, attn_d128.hip
+// and attn_d512.hip).
 //
 // Page "HCCL AllGatherV 实战解析：MiniMax-H3-Comfy-NPU ...", section 机制一: the
 // local shard provides Q, K/V span the whole sequence, no mask.  Scale 1/sqrt(d)
@@ -39,11 +42,11 @@
 //    of tile t follows.  The loop is unrolled by two so the two S^T register
 //    sets alternate roles without copies.
 //  * Work-groups are ordered head-major, so at any time all XCDs work on the
-//    same head: its K+V (188 MB at 367k tokens) stays in the 256 MB Infinity
-//    Cache and each XCD's L2 serves its co-resident query tiles.
-//  * Head sizes 64 and 128.  Head size 512 (the VAE's single-head attention)
-//    has a kernel of its own (attn_d512.hip), since its accumulators and Q
-//    fragments do not fit this layout.
+//    same head: its K+V stays in the 256 MB Infinity Cache and each XCD's L2
+//    serves its co-resident query tiles.
+//  * Head size 64.  (This layout also ran head size 128 at one wave per SIMD;
+//    the eight-wave kernel of attn_d128.hip, two waves per SIMD with one
+//    wave's softmax under the other's MFMAs, replaced it there.)
 // Per output row the arithmetic depends only on that query row and on K/V in
 // a fixed key order, so results are deterministic and independent of sq and
 // of the row's position inside a tile.
@@ -100,11 +103,11 @@ constexpr float kTau = 8.0f;           // lazy-rescale threshold (log2 units)
 constexpr float kCheck = 256.0f;       // 2^kTau: a lane's block sum above it triggers the reference check
 constexpr float kLn2 = 0.69314718055994531f;
 
-// Shape of the kernel for head size D (64 or 128): two 32-query blocks per
-// wave (QB), 64-key tiles, every output column.
+// Shape of the kernel for head size D (64): two 32-query blocks per wave
+// (QB), 64-key tiles, every output column.
 template <int D>
 struct Geo {
-  static_assert(D == 64 || D == 128, "head sizes 64 and 128");
+  static_assert(D == 64, "head size 64 (128 and 512 have kernels of their own)");
   static constexpr int kD = D;
   static constexpr int QB = SPATTN_QB;                    // 32-query MFMA blocks per wave
   static constexpr int BM = kWaves * 32 * QB;             // query rows per work-group
@@ -938,7 +941,8 @@ hipError_t launch_split(const void* q, const void* k, const void* v, void* o, fl
 
 int64_t attn_bf16_items(int64_t sq, int H, int d, int nsplit) {
   if (d == 512) return attn_d512_items(sq, H, nsplit);
-  const int bm = Geo<128>::BM;
+  if (d == 128) return attn_d128_items(sq, H, nsplit);
+  const int bm = Geo<64>::BM;
   const __int128 n = __int128((sq + bm - 1) / bm) * H * nsplit * kThreads;
   return n > INT64_MAX ? INT64_MAX : int64_t(n);
 }
@@ -955,7 +959,7 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o
   const KvFlat kv{static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v)};
   if (d == 64) return launch_d<64, false>(q, kv, o, lse, sq, skv, H, c, stream);
   if (d == 512) return launch_attn_d512(q, k, v, o, lse, sq, skv, H, c, 1, nullptr, stream);
-  return launch_d<128, false>(q, kv, o, lse, sq, skv, H, c, stream);
+  return launch_attn_d128(q, k, v, o, lse, sq, skv, H, c, 1, nullptr, stream);
 }
 
 hipError_t launch_attn_bf16_gv(const void* q, const KvShards& kv, void* o, float* lse, int64_t sq, int H, int d,
@@ -964,7 +968,7 @@ hipError_t launch_attn_bf16_gv(const void* q, const KvShards& kv, void* o, float
   const float c = scale * 1.4426950408889634f;
   const int64_t skv = kv.start[kv.W];
   if (d == 64) return launch_d<64, true>(q, kv, o, lse, sq, skv, H, c, stream);
-  return launch_d<128, true>(q, kv, o, lse, sq, skv, H, c, stream);
+  return launch_attn_d128_gv(q, kv, o, lse, sq, H, c, stream);
 }
 
 namespace {
@@ -1004,14 +1008,14 @@ hipError_t launch_attn_bf16_split(const void* q, const void* k, const void* v, v
   if (sq > (int64_t(1) << 31) - 1024) return hipErrorInvalidValue;
   const float c = scale * 1.4426950408889634f;
   if (d == 64) return launch_split<64>(q, k, v, o, lse, sq, skv, H, c, nsplit, opart, lpart, stream);
-  if (d == 512) {
-    if (attn_d512_items(sq, H, nsplit) > kMaxItems || attn_merge_items(sq, H, d) > kMaxItems)
-      return hipErrorInvalidConfiguration;
-    hipError_t e = launch_attn_d512(q, k, v, o, lpart, sq, skv, H, c, nsplit, opart, stream);
-    if (e != hipSuccess) return e;
-    return launch_merge(opart, lpart, o, lse, nsplit, sq, H, d, stream);
-  }
-  return launch_split<128>(q, k, v, o, lse, sq, skv, H, c, nsplit, opart, lpart, stream);
+  // Both grids are checked before the first launch, so a call that does not
+  // fit enqueues nothing.
+  if (attn_bf16_items(sq, H, d, nsplit) > kMaxItems || attn_merge_items(sq, H, d) > kMaxItems)
+    return hipErrorInvalidConfiguration;
+  hipError_t e = d == 512 ? launch_attn_d512(q, k, v, o, lpart, sq, skv, H, c, nsplit, opart, stream)
+                          : launch_attn_d128(q, k, v, o, lpart, sq, skv, H, c, nsplit, opart, stream);
+  if (e != hipSuccess) return e;
+  return launch_merge(opart, lpart, o, lse, nsplit, sq, H, d, stream);
 }
 
 }  // namespace spattn

@@ -79,6 +79,15 @@ hipError_t launch_attn_d512(const void* q, const void* k, const void* v, void* o
                             int64_t skv, int H, float c, int nsplit, float* opart, hipStream_t stream);
 int64_t attn_d512_items(int64_t sq, int H, int nsplit);
 
+// Head size 128 (bf16, eight waves per work-group, two per SIMD).  c is the
+// softmax scale times log2(e).  opart == nullptr: writes o and lse (may be
+// null); otherwise key ranges and float32 partials as launch_attn_d512.
+hipError_t launch_attn_d128(const void* q, const void* k, const void* v, void* o, float* lse, int64_t sq,
+                            int64_t skv, int H, float c, int nsplit, float* opart, hipStream_t stream);
+hipError_t launch_attn_d128_gv(const void* q, const KvShards& kv, void* o, float* lse, int64_t sq, int H, float c,
+                               hipStream_t stream);
+int64_t attn_d128_items(int64_t sq, int H, int nsplit);
+
 // Device scratch of the split attention's allocation-free entry point: one
 // file-scope array per device (kScratchBytes, 256-byte aligned), held until
 // the process ends.  scratch_address() gives the current device's copy; the

@@ -24,7 +24,7 @@ LIB = os.path.join(OUT_DIR, "libspattn_asan.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = shutil.which("hipcc") or f"{ROCM}/bin/hipcc"
 CLANGXX = f"{ROCM}/llvm/bin/clang++"
-KERNEL_OBJS = ["attn_bf16.hip.o", "attn_d512.hip.o", "attn_f32.hip.o", "pack.hip.o", "rope.hip.o"]
+KERNEL_OBJS = ["attn_bf16.hip.o", "attn_d128.hip.o", "attn_d512.hip.o", "attn_f32.hip.o", "pack.hip.o", "rope.hip.o"]
 
 
 def runtime() -> str:

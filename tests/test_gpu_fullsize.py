@@ -59,11 +59,12 @@ def test_fullsize_rank_share(name):
     torch.cuda.synchronize()
     a, b = share.a, share.b
     # 32 sampled rows (first/last, 128-row tile edges, random), plus both sides of 24 work-group
-    # boundaries (every 256 query rows form one work-group) spread evenly over the shard, and the
-    # first and last rows of the final, partial work-group
+    # boundaries (every 512 query rows form one work-group of the head-size-128 kernel, every 256
+    # one of 64 rows per wave) spread evenly over the shard, and the first and last rows of the
+    # final, partial work-group
     n = b - a
     wg = np.unique(np.linspace(1, max(1, (n - 1) // 256), 24).astype(np.int64)) * 256
-    edges = np.concatenate([wg - 1, wg, [((n - 1) // 256) * 256, n - 1]])
+    edges = np.concatenate([wg - 1, wg, [((n - 1) // 512) * 512, ((n - 1) // 256) * 256, n - 1]])
     rows = np.unique(np.concatenate([sample_rows(n, 32, seed=wl.seed), edges[(edges >= 0) & (edges < n)]]))
     rows_abs = rows + a
     _log(f"{name}: GPU done; oracle on {len(rows)} rows x {wl.H} heads")
