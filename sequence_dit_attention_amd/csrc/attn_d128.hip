@@ -235,13 +235,16 @@ __global__ __launch_bounds__(kThreads) void attn_d128_kernel(const uint16_t* __r
   const bool ragged = (skv % kBN) != 0;
 
   // ---- tile loads (waves 0..3): wave w fills 1 KiB blocks w and w + 4 of the
-  // K tile and of the V tile.  K block b holds rows 8(b>>1) .. +8, chunks
-  // 8(b&1) .. +8 at 16-byte position (chunk & 7) * 8 + (row & 7); V block b
-  // holds rows 4b .. 4b+3, chunk 4g + e of row a at position 16g + 8(e>>1) +
-  // 2a + (e&1).  Block w + 4 is block w sixteen rows down.
+  // K tile and of the V tile.  K block b holds rows 8R .. 8R+7 (R = b>>1),
+  // chunks 8(b&1) .. +8 at 16-byte position ((chunk & 7) ^ (R & 1)) * 8 +
+  // (row & 7): the 16 lanes that the LDS serves together (rows 8R .. 8R+15 of
+  // one chunk) then cover all 64 banks once.  V block b holds rows 4b .. 4b+3,
+  // chunk 4g + e of row a at position 16g + 8(e>>1) + 2a + (e&1).  Block w + 4
+  // is block w sixteen rows down.
   const int rowK = 8 * (wave >> 1) + (lane & 7);
   const int rowV = 4 * wave + ((lane >> 1) & 3);
-  const uint32_t voffK = uint32_t(rowK) * rowbytes + uint32_t(8 * (wave & 1) + (lane >> 3)) * 16u;
+  const uint32_t voffK =
+      uint32_t(rowK) * rowbytes + uint32_t(8 * (wave & 1) + ((lane >> 3) ^ ((wave >> 1) & 1))) * 16u;
   const uint32_t voffV =
       uint32_t(rowV) * rowbytes + uint32_t(4 * (lane >> 4) + 2 * ((lane >> 3) & 1) + (lane & 1)) * 16u;
   // Sharded K/V: a cursor on the shard that holds the last tile's first key
@@ -333,11 +336,12 @@ __global__ __launch_bounds__(kThreads) void attn_d128_kernel(const uint16_t* __r
   }
   f32x16 s[kQB];  // a step's scores; then its probability words (in place)
 
-  // Per-lane LDS operand bases: K row `col`, chunk 2cc + hf; V^T rows
+  // Per-lane LDS operand bases: K row `col`, chunk 2cc + hf (position bit 0
+  // flipped in odd 8-row groups); V^T rows
   // 16u + 4hf + (j16 >> 2) (+8 for the second read), columns 32db + 16(g16&1)
   // + 4(j16&3).
   const char* const lds = smem;
-  const uint32_t kl = uint32_t((col >> 3) * 2048 + hf * 128 + (col & 7) * 16);
+  const uint32_t kl = uint32_t((col >> 3) * 2048 + (hf ^ ((col >> 3) & 1)) * 128 + (col & 7) * 16);
   const int g16 = lane >> 4, j16 = lane & 15;
   const uint32_t vl = uint32_t(hf * 1024 + 128 * (g16 & 1) + 32 * (j16 >> 2) + 8 * (j16 & 3));
   auto kread = [&](const char* kb, int cc) {
