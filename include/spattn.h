@@ -331,7 +331,8 @@ int shard_attn_fwd(int32_t dtype, const void* q, const void* k, const void* v,
  * fill the GPU (the single-head attention of the VAE block split, page "NPU
  * HunyuanImage-3.0模型推理优化实践", section VAE并行优化, has one head and a
  * few thousand queries per process).  Range s covers whole key tiles
- * [T*s/nsplit, T*(s+1)/nsplit) of the T tiles; each range yields its own
+ * [T*s/nsplit, T*(s+1)/nsplit) of the T tiles (32 keys each at head sizes
+ * 128 and 512, 64 at head size 64); each range yields its own
  * normalised float32 output O_s and log-sum-exp L_s, and the results are
  * combined exactly as the softmax over the union of the ranges:
  *   O = sum_s exp(L_s - M) O_s / sum_s exp(L_s - M),  LSE = M + log sum_s exp(L_s - M)
