@@ -15,7 +15,9 @@
 //    fragments (64 registers) and O accumulators (128) in VGPRs for the whole
 //    key loop.  At two waves per SIMD a wave has 256 registers in all; the
 //    compiler splits the register file evenly between VGPRs and AGPRs as soon
-//    as a kernel uses AGPRs, so every MFMA here is inline asm on VGPRs.
+//    as a kernel uses AGPRs, so every MFMA here is inline asm on VGPRs.  Calls
+//    whose 512-row grid would leave CUs idle run 32 rows per wave (256 per
+//    work-group) instead; a row's arithmetic is the same in both.
 //  * Each 32-key step of a wave has an MFMA phase (P*V of the previous step,
 //    then the scores S^T = K Q^T of this step: 32 MFMAs of 32x32x16) and a
 //    softmax phase (VALU).  Waves 4..7 run half a step behind waves 0..3, with
@@ -72,8 +74,9 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 constexpr int kD = 128;
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kQB = 2;                     // 32-query MFMA blocks per wave
-constexpr int kBM = kWaves * 32 * kQB;     // query rows per work-group
+// 32-query MFMA blocks per wave: 2 (512 query rows per work-group), or 1
+// (256 rows) for calls whose 512-row grid would leave CUs idle.
+constexpr int kCUs = 256;                  // compute units of an MI355X
 constexpr int kBN = 32;                    // keys per step (one K tile, one V tile)
 constexpr int kTileB = kBN * kD * 2;       // bytes of a K or V tile
 constexpr int kSetB = 2 * kTileB;          // a slot: K tile, then V tile
@@ -158,9 +161,10 @@ __device__ inline void mfma_last(f32x16& d, const bf16x8& a, const bf16x8& b) {
 }
 
 // Maximum of a step's scores per query column (both wave halves), log2 units.
-__device__ inline void step_max(const f32x16 (&s)[kQB], float (&mt)[kQB], float c) {
+template <int QB>
+__device__ inline void step_max(const f32x16 (&s)[QB], float (&mt)[QB], float c) {
 #pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     float m = fmaxf(s[qb][0], s[qb][1]);
 #pragma unroll
     for (int r = 2; r < 16; r += 2) m = max3(m, s[qb][r], s[qb][r + 1]);
@@ -172,8 +176,9 @@ __device__ inline void step_max(const f32x16 (&s)[kQB], float (&mt)[kQB], float 
 // packed to bf16 in place at s[qb][8(pr>>2) + (pr&3)] (the words of 16-key
 // half u then fill s[qb][8u .. 8u+3], the B operand of its P*V MFMA); the two
 // float32 probabilities are added to the lane's row sum.
-__device__ __attribute__((always_inline)) inline void prob_word(f32x16 (&s)[kQB], const float (&m)[kQB], float c,
-                                                               int qb, int pr, float (&ls)[kQB]) {
+template <int QB>
+__device__ __attribute__((always_inline)) inline void prob_word(f32x16 (&s)[QB], const float (&m)[QB], float c,
+                                                               int qb, int pr, float (&ls)[QB]) {
   const float p0 = __builtin_amdgcn_exp2f(fmaf(s[qb][2 * pr], c, -m[qb]));
   const float p1 = __builtin_amdgcn_exp2f(fmaf(s[qb][2 * pr + 1], c, -m[qb]));
   s[qb][8 * (pr >> 2) + (pr & 3)] = __builtin_bit_cast(float, pack_bf16x2(p0, p1));
@@ -191,11 +196,12 @@ using KvArg = typename std::conditional<GV, KvShards, KvFlat>::type;
 // ranges of whole 32-key tiles; the work-group of range sp writes its float32
 // O normalised over its own keys (opart [nsplit, sq, H, 128]) and the range's
 // LSE (lse [nsplit, H, sq]).
-template <bool GV, bool SPLIT>
+template <int QB, bool GV, bool SPLIT>
 __global__ __launch_bounds__(kThreads) void attn_d128_kernel(const uint16_t* __restrict__ q, const KvArg<GV> kv,
                                                              uint16_t* __restrict__ o, float* __restrict__ lse,
                                                              int sq, int skv_all, int H, float c, int nqt,
                                                              int nsplit, float* __restrict__ opart) {
+  constexpr int BM = kWaves * 32 * QB;  // query rows per work-group
   __shared__ __attribute__((aligned(1024))) char smem[kSlots * kSetB];
   const uint32_t sbase = uint32_t(reinterpret_cast<uintptr_t>(smem));
 
@@ -309,10 +315,10 @@ __global__ __launch_bounds__(kThreads) void attn_d128_kernel(const uint16_t* __r
 
   // Q fragments (B operand of S^T = K Q^T): lane holds 8 channels of one
   // query per k-step; rows past sq read zeros and are never written.
-  bf16x8 qf[kQB][kDC];
-  const int qrow0 = qt * kBM + wave * 32 * kQB;
+  bf16x8 qf[QB][kDC];
+  const int qrow0 = qt * BM + wave * 32 * QB;
 #pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     const int row = qrow0 + qb * 32 + col;
     const u32x4* src = reinterpret_cast<const u32x4*>(q + int64_t(row) * rowstride + int64_t(h) * kD + 8 * hf);
 #pragma unroll
@@ -321,20 +327,20 @@ __global__ __launch_bounds__(kThreads) void attn_d128_kernel(const uint16_t* __r
       qf[qb][cc] = __builtin_bit_cast(bf16x8, t);
     }
   }
-  f32x16 acc[kND][kQB];  // O^T: [32-row block of the head dimension][query block]
+  f32x16 acc[kND][QB];  // O^T: [32-row block of the head dimension][query block]
 #pragma unroll
   for (int db = 0; db < kND; ++db)
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[db][qb][r] = 0.f;
-  float m_run[kQB], l_run[kQB];  // reference (log2 units; both halves), the lane's partial row sum
+  float m_run[QB], l_run[QB];  // reference (log2 units; both halves), the lane's partial row sum
 #pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     m_run[qb] = 0.f;
     l_run[qb] = 0.f;
   }
-  f32x16 s[kQB];  // a step's scores; then its probability words (in place)
+  f32x16 s[QB];  // a step's scores; then its probability words (in place)
 
   // Per-lane LDS operand bases: K row `col`, chunk 2cc + hf (position bit 0
   // flipped in odd 8-row groups); V^T rows
@@ -365,7 +371,7 @@ __global__ __launch_bounds__(kThreads) void attn_d128_kernel(const uint16_t* __r
       if (cc + 1 < kDC) kf[(cc + 1) & 1] = kread(kb, cc + 1);
       const bf16x8 a = kf[cc & 1];
 #pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) {
+      for (int qb = 0; qb < QB; ++qb) {
         if (cc == 0) mfma_first(s[qb], a, qf[qb][cc]);
         else if (cc + 1 < kDC) mfma_acc(s[qb], a, qf[qb][cc]);
         else mfma_last(s[qb], a, qf[qb][cc]);
@@ -375,7 +381,7 @@ __global__ __launch_bounds__(kThreads) void attn_d128_kernel(const uint16_t* __r
     if (mask) {
       const int key_last = skv - t * kBN;
 #pragma unroll
-      for (int qb = 0; qb < kQB; ++qb)
+      for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           if (8 * (r >> 2) + 4 * hf + (r & 3) >= key_last) s[qb][r] = -INFINITY;
@@ -395,7 +401,7 @@ __global__ __launch_bounds__(kThreads) void attn_d128_kernel(const uint16_t* __r
       else if (pre_k) kf[0] = kread(kbn, 0);
       const bf16x8 a = vf[kk & 1];
 #pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) {
+      for (int qb = 0; qb < QB; ++qb) {
         const f32x4 w = u == 0 ? __builtin_shufflevector(s[qb], s[qb], 0, 1, 2, 3)
                                : __builtin_shufflevector(s[qb], s[qb], 8, 9, 10, 11);
         mfma_acc(acc[db][qb], a, __builtin_bit_cast(bf16x8, w));
@@ -407,23 +413,23 @@ __global__ __launch_bounds__(kThreads) void attn_d128_kernel(const uint16_t* __r
   // maximum becomes the reference (every column has a key in the first step).
   auto softmax = [&](int t, bool first, bool mask) __attribute__((always_inline)) {
     if (first) step_max(s, m_run, c);
-    float ls[kQB];
+    float ls[QB];
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
       ls[qb] = 0.f;
 #pragma unroll
       for (int pr = 0; pr < 8; ++pr) prob_word(s, m_run, c, qb, pr, ls);
     }
     bool need = false;
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) need |= ls[qb] > kCheck;  // an overflow to inf included
+    for (int qb = 0; qb < QB; ++qb) need |= ls[qb] > kCheck;  // an overflow to inf included
     if (__builtin_amdgcn_ballot_w64(need) != 0) {
       bf16x8 kf[2];
       scores(t, mask, kf, false);  // the words replaced the scores: form them again
-      float mt[kQB], alpha[kQB];
+      float mt[QB], alpha[QB];
       step_max(s, mt, c);
 #pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) {
+      for (int qb = 0; qb < QB; ++qb) {
         const float m_new = mt[qb] > m_run[qb] + kTau ? mt[qb] : m_run[qb];
         alpha[qb] = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
         m_run[qb] = m_new;
@@ -433,14 +439,14 @@ __global__ __launch_bounds__(kThreads) void attn_d128_kernel(const uint16_t* __r
 #pragma unroll
       for (int db = 0; db < kND; ++db)
 #pragma unroll
-        for (int qb = 0; qb < kQB; ++qb) acc[db][qb] *= alpha[qb];
+        for (int qb = 0; qb < QB; ++qb) acc[db][qb] *= alpha[qb];
 #pragma unroll
-      for (int qb = 0; qb < kQB; ++qb)
+      for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int pr = 0; pr < 8; ++pr) prob_word(s, m_run, c, qb, pr, ls);
     }
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) l_run[qb] += ls[qb];
+    for (int qb = 0; qb < QB; ++qb) l_run[qb] += ls[qb];
   };
 
   // ---- phases.  Phase p ends with barrier p.  Waves 0..3: phase 2t is the
@@ -496,7 +502,7 @@ __global__ __launch_bounds__(kThreads) void attn_d128_kernel(const uint16_t* __r
 
   // ---- epilogue: O = O^T / l, rows past sq are dropped
 #pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     const float lt = halves_sum(l_run[qb]);
     const float inv = 1.f / lt;
     const int row = qrow0 + qb * 32 + col;
@@ -529,23 +535,40 @@ __global__ __launch_bounds__(kThreads) void attn_d128_kernel(const uint16_t* __r
   }
 }
 
-template <bool GV, bool SPLIT>
-hipError_t launch(const void* q, const KvArg<GV>& kv, void* o, float* lse, int64_t sq, int64_t skv, int H, float c,
-                  int nsplit, float* opart, hipStream_t stream) {
-  if (sq < 1) return hipSuccess;
-  const int64_t nqt = (sq + kBM - 1) / kBM;
+// One 32-query block per wave when the 512-row grid would not give every CU
+// a work-group; a row's arithmetic is the same either way.
+int blocks_per_wave(int64_t sq, int H, int nsplit) {
+  const int64_t wg2 = (sq + kWaves * 64 - 1) / (kWaves * 64) * H * nsplit;
+  return wg2 < kCUs ? 1 : 2;
+}
+
+template <int QB, bool GV, bool SPLIT>
+hipError_t launch_qb(const void* q, const KvArg<GV>& kv, void* o, float* lse, int64_t sq, int64_t skv, int H,
+                     float c, int nsplit, float* opart, hipStream_t stream) {
+  constexpr int BM = kWaves * 32 * QB;
+  const int64_t nqt = (sq + BM - 1) / BM;
   const int64_t grid = nqt * H * nsplit;  // the host has checked grid * kThreads <= kMaxItems
   if (grid > kMaxItems / kThreads) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((attn_d128_kernel<GV, SPLIT>), dim3(unsigned(grid)), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((attn_d128_kernel<QB, GV, SPLIT>), dim3(unsigned(grid)), dim3(kThreads), 0, stream,
                      static_cast<const uint16_t*>(q), kv, static_cast<uint16_t*>(o), lse, int(sq), int(skv), H, c,
                      int(nqt), nsplit, opart);
   return hipGetLastError();
 }
 
+template <bool GV, bool SPLIT>
+hipError_t launch(const void* q, const KvArg<GV>& kv, void* o, float* lse, int64_t sq, int64_t skv, int H, float c,
+                  int nsplit, float* opart, hipStream_t stream) {
+  if (sq < 1) return hipSuccess;
+  if (blocks_per_wave(sq, H, nsplit) == 1)
+    return launch_qb<1, GV, SPLIT>(q, kv, o, lse, sq, skv, H, c, nsplit, opart, stream);
+  return launch_qb<2, GV, SPLIT>(q, kv, o, lse, sq, skv, H, c, nsplit, opart, stream);
+}
+
 }  // namespace
 
 int64_t attn_d128_items(int64_t sq, int H, int nsplit) {
-  const __int128 n = __int128((sq + kBM - 1) / kBM) * H * nsplit * kThreads;
+  const int64_t bm = kWaves * 32 * blocks_per_wave(sq, H, nsplit);
+  const __int128 n = __int128((sq + bm - 1) / bm) * H * nsplit * kThreads;
   return n > INT64_MAX ? INT64_MAX : int64_t(n);
 }
 
