@@ -373,8 +373,8 @@ __global__ __launch_bounds__(kThreads) void attn_d128_kernel(const uint16_t* __r
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         if (cc == 0) mfma_first(s[qb], a, qf[qb][cc]);
-        else if (cc + 1 < kDC) mfma_acc(s[qb], a, qf[qb][cc]);
-        else mfma_last(s[qb], a, qf[qb][cc]);
+        else if (cc + 1 < kDC || qb + 1 < QB) mfma_acc(s[qb], a, qf[qb][cc]);
+        else mfma_last(s[qb], a, qf[qb][cc]);  // its wait states also cover the other block's last MFMA
       }
       __builtin_amdgcn_sched_barrier(0);
     }
