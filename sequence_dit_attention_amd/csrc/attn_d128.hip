@@ -254,9 +254,17 @@ __global__ __launch_bounds__(kThreads) void attn_d128_kernel(const uint16_t* __r
   const uint32_t voffV =
       uint32_t(rowV) * rowbytes + uint32_t(4 * (lane >> 4) + 2 * ((lane >> 3) & 1) + (lane & 1)) * 16u;
   // Sharded K/V: a cursor on the shard that holds the last tile's first key
-  // (tiles are loaded in increasing order; empty shards are stepped over).
+  // (tiles are loaded in increasing order; empty shards are stepped over),
+  // with that shard's K and V bases for head h, read from the kernel
+  // arguments only when the cursor moves.
   int cr = 0, cs0 = 0, cs1 = 0;
-  if constexpr (GV) cs1 = int(kv.start[1]);
+  const char* ck = nullptr;
+  const char* cv = nullptr;
+  if constexpr (GV) {
+    cs1 = int(kv.start[1]);
+    ck = static_cast<const char*>(kv.k[0]) + hoff;
+    cv = static_cast<const char*>(kv.v[0]) + hoff;
+  }
   // Tile set j = K and V tile j into slot j mod kSlots; indices past the last
   // tile reload it (those sets land in slots no live step reads, and every
   // step issues the same number of loads for the vmcnt accounting).
@@ -281,6 +289,8 @@ __global__ __launch_bounds__(kThreads) void attn_d128_kernel(const uint16_t* __r
         ++cr;
         cs0 = cs1;
         cs1 = int(kv.start[cr + 1]);
+        ck = static_cast<const char*>(kv.k[cr]) + hoff;
+        cv = static_cast<const char*>(kv.v[cr]) + hoff;
       }
       if (key0 + valid > cs1) {  // the tile spans shards: every lane finds its row's shard
 #pragma unroll
@@ -296,8 +306,8 @@ __global__ __launch_bounds__(kThreads) void attn_d128_kernel(const uint16_t* __r
         }
         return;
       }
-      kb = static_cast<const char*>(kv.k[cr]) + hoff + int64_t(key0 - cs0) * rowbytes;
-      vb = static_cast<const char*>(kv.v[cr]) + hoff + int64_t(key0 - cs0) * rowbytes;
+      kb = ck + int64_t(key0 - cs0) * rowbytes;
+      vb = cv + int64_t(key0 - cs0) * rowbytes;
     } else {
       kb += int64_t(key0) * rowbytes;
       vb += int64_t(key0) * rowbytes;
