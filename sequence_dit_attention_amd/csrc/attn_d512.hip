@@ -14,13 +14,22 @@
 //   * wave w forms the scores S^T = K Q^T of query block w (32 queries) over
 //     the tile's 32 keys and their softmax, and writes the bf16 probabilities
 //     (already in the B-operand layout of the P*V MFMA) to LDS;
-//   * after a barrier, wave w accumulates output columns [128w, 128w + 128)
-//     for all four query blocks, reading P from LDS and V^T from the tile.
+//   * wave w accumulates output columns [128w, 128w + 128) for all four
+//     query blocks, reading P from LDS and V^T from the tile.
 // So every score is formed once, a lane holds 128 Q registers (VGPRs) and 256
 // accumulators (4 blocks x 4 column tiles x 16, all the AGPRs), and each K
 // operand read from LDS feeds one MFMA, each V^T operand four.  Per 32 keys
 // and 128 queries: 256 MFMAs of 32x32x16 against 160 KiB of LDS operand reads
 // and 64 KiB of tile writes.
+//
+// Software pipeline, one barrier per tile: a wave computes the scores of tile
+// t, then makes their probabilities while its P*V MFMAs of tile t-1 run (the
+// probabilities of tile t-1 are in LDS since the previous barrier), writes
+// them to the other of two P buffers, and meets the other waves.  K tile t+1
+// loads during tile t into the slot K tile t-1 used; V tile t loads during
+// tile t into the slot of V tile t-2, which the P*V of tile t-1 does not read.
+// Row sums add the two bf16 halves of each probability word as float32 (the
+// weights P*V uses, exactly; v_dot2 would wait for the wave's MFMAs).
 //
 // Softmax: float32, base 2 with the scale folded into log2(e).  The O
 // accumulators are never rescaled (as C++ on AGPR values, a rescale would make
@@ -34,8 +43,8 @@
 // Each restart is caused by a later tile than the previous one, so there are
 // at most as many restarts as tiles.
 //
-// K and V tiles stream through LDS with LDS-direct loads (no VGPR staging),
-// one tile ahead.  LDS rows are padded (K 1040 bytes, V 1088) rather than
+// K and V tiles stream through LDS with LDS-direct loads (no VGPR staging).
+// LDS rows are padded (K 1040 bytes, V 1088) rather than
 // swizzled, so every operand read is one per-lane base plus an immediate
 // offset; the padding spreads the rows that one read touches over the banks.
 #include <stdint.h>
@@ -79,9 +88,10 @@ constexpr int kKSlotB = kBN * kKS;
 constexpr int kVSlotB = kBN * kVS;
 constexpr int kOffK = 0;
 constexpr int kOffV = 2 * kKSlotB;
-constexpr int kOffP = kOffV + 2 * kVSlotB;             // [block][u][lane] 16 bytes
-constexpr int kOffF = kOffP + kWaves * 2 * 64 * 16;    // int flag[block]
-constexpr int kOffL = kOffF + 16;                      // float lsum[block][32]
+constexpr int kPB = kWaves * 2 * 64 * 16;             // probabilities of one tile: [block][u][lane] 16 bytes
+constexpr int kOffP = kOffV + 2 * kVSlotB;             // two tiles' probabilities
+constexpr int kOffF = kOffP + 2 * kPB;                 // int flag[tile & 1][block]
+constexpr int kOffL = kOffF + 32;                      // float lsum[block][32]
 constexpr int kSmem = kOffL + kWaves * 32 * 4;
 static_assert(kSmem <= 160 * 1024, "LDS");
 
@@ -132,39 +142,6 @@ __device__ inline void lds_load(const i32x4& rs, uint32_t m0, uint32_t soffset, 
 __device__ inline i32x4 rsrc(const char* base) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
   return i32x4{int(uint32_t(a)), int(uint32_t(a >> 32) & 0xFFFF), 0x7FFFFFFF, 0x00020000};
-}
-
-// Loads tile rows [8w, 8w + 8) of K and of V; rows past `valid` re-read row
-// valid-1 (finite data for keys that are masked to -inf).  Everything but the
-// lane's byte offset is wave-uniform.
-__device__ inline void load_tile(const char* kt, const char* vt, int valid, uint32_t rowbytes, uint32_t kslot,
-                                 uint32_t vslot, int wave, uint32_t lane16) {
-  const i32x4 rk = rsrc(kt), rv = rsrc(vt);
-#pragma unroll
-  for (int j = 0; j < kRowsW; ++j) {
-    const int r = wave * kRowsW + j;
-    const uint32_t so = uint32_t(r < valid ? r : valid - 1) * rowbytes;
-    lds_load(rk, kslot + r * kKS, so, lane16);
-    lds_load(rv, vslot + r * kVS, so, lane16);
-  }
-}
-
-// Probabilities of the wave's 32 x 32 score block under reference m (per
-// query column, log2 units): w[u][e] packs scores r = 8u + 2e, 8u + 2e + 1 of
-// the lane's accumulator (B operand of P*V MFMA u); returns the lane's sum of
-// the 16 bf16 probabilities.
-__device__ inline float make_words(const f32x16& s, float c, float m, uint32_t (&w)[2][4]) {
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  float ls = 0.f;
-#pragma unroll
-  for (int pr = 0; pr < 8; ++pr) {
-    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[2 * pr], c, -m));
-    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[2 * pr + 1], c, -m));
-    const uint32_t word = pack_bf16x2(p0, p1);
-    w[pr >> 2][pr & 3] = word;
-    ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, word), ones, ls, false);
-  }
-  return ls;
 }
 
 // Score MFMAs.  The O accumulators take all 256 AGPRs (the P*V MFMAs are
@@ -243,7 +220,18 @@ __global__ __launch_bounds__(kThreads) void attn_d512_kernel(const uint16_t* __r
 
   auto kslot = [&](int j) { return sbase + kOffK + (unsigned(j) & 1u) * kKSlotB; };
   auto vslot = [&](int j) { return sbase + kOffV + (unsigned(j) & 1u) * kVSlotB; };
-  load_tile(kh, vh, min(skv, kBN), rowbytes, kslot(0), vslot(0), wave, lane16);
+  // This wave's rows [8w, 8w + 8) of K tile j or V tile j; rows past the
+  // range re-read its last row (finite data for keys that are masked).
+  auto load_rows = [&](const char* base, int j, uint32_t slot, int stride) __attribute__((always_inline)) {
+    const i32x4 rs = rsrc(base + int64_t(j) * tb);
+    const int valid = min(skv - j * kBN, kBN);
+#pragma unroll
+    for (int jj = 0; jj < kRowsW; ++jj) {
+      const int r = wave * kRowsW + jj;
+      lds_load(rs, slot + r * stride, uint32_t(r < valid ? r : valid - 1) * rowbytes, lane16);
+    }
+  };
+  load_rows(kh, 0, kslot(0), kKS);
 
   // Q fragments of this wave's query block (B operand of S^T = K Q^T): lane
   // holds 8 channels of query `col` per k-step.  Rows past sq repeat row
@@ -274,14 +262,41 @@ __global__ __launch_bounds__(kThreads) void attn_d512_kernel(const uint16_t* __r
   const int g16 = lane >> 4, j16 = lane & 15;
   const uint32_t koff = uint32_t(col * kKS + hf * 16);
   const uint32_t voff = uint32_t((4 * hf + (j16 >> 2)) * kVS + (wave * kColsW + 16 * (g16 & 1) + 4 * (j16 & 3)) * 2);
+  auto pread = [&](int t, int b, int u) {
+    return *reinterpret_cast<const bf16x8*>(smem + kOffP + (unsigned(t) & 1u) * kPB + ((b * 2 + u) * 64 + lane) * 16);
+  };
+  // V^T operand of MFMA u, column tile ct of tile t: channels [32 ct, 32 ct + 32)
+  // of this wave x the 16 keys of u, in the key order of the probability words.
+  auto vread = [&](int t, int u, int ct) {
+    const char* p0 = lds + (vslot(t) - sbase) + voff + u * 16 * kVS + ct * 64;
+    const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
+    const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 8 * kVS));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  // O^T[cols of this wave][queries of block b] += V^T P^T, MFMA group g (16-key
+  // half u = g / kCT, column tile ct = g % kCT) of tile t; pf holds P(u).
+  auto pv_group = [&](int t, int g, bf16x8 (&pf)[kWaves]) __attribute__((always_inline)) {
+    const int u = g / kCT, ct = g % kCT;
+    if (ct == 0) {
+#pragma unroll
+      for (int b = 0; b < kWaves; ++b) pf[b] = pread(t, b, u);
+    }
+    const bf16x8 vc = vread(t, u, ct);
+#pragma unroll
+    for (int b = 0; b < kWaves; ++b)
+      acc[b][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vc, pf[b], acc[b][ct], 0, 0, 0);
+  };
+  constexpr int kGroups = 2 * kCT;  // MFMA groups of a tile's P*V
 
+  // Tile t: the scores of this wave's block; then, under the P*V MFMAs of
+  // tile t-1, their softmax; the probabilities and the raise flag to LDS; one
+  // barrier.  K tile t+1 and V tile t load during the tile (K tile t+1 into
+  // the slot of K tile t-1, read before the last barrier; V tile t into that
+  // of V tile t-2, read during tile t-1).
   for (int t = 0; t < nT; ++t) {
-    barrier_wait<0>();  // tile t has landed; every wave is done with tile t-1
-    if (t + 1 < nT)
-      load_tile(kh + (t + 1) * tb, vh + (t + 1) * tb, min(skv - (t + 1) * kBN, kBN), rowbytes, kslot(t + 1),
-                vslot(t + 1), wave, lane16);
+    if (t + 1 < nT) load_rows(kh, t + 1, kslot(t + 1), kKS);
+    load_rows(vh, t, vslot(t), kVS);
     const char* kb = lds + (kslot(t) - sbase) + koff;
-    const char* vb = lds + (vslot(t) - sbase) + voff;
 
     // ---- scores of this wave's query block over the tile's 32 keys; the K
     // operands are read kKRA MFMAs ahead, each read-MFMA pair fenced in order
@@ -309,24 +324,46 @@ __global__ __launch_bounds__(kThreads) void attn_d512_kernel(const uint16_t* __r
       }
     }
 
-    // ---- softmax of the block; probabilities to LDS for every wave
-    uint32_t w[2][4];
+    // ---- softmax of the block (float32 row sums: v_dot2 would wait for the
+    // MFMA pipe) under the P*V of tile t-1
     if (t == 0) m_run = fmaxf(m_run, col_max(s, c) + kOff);  // every column has a key in the first tile
-    const float ls = make_words(s, c, m_run, w);
+    uint32_t w[2][4];
+    float ls = 0.f;
+    auto word = [&](int pr) __attribute__((always_inline)) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[2 * pr], c, -m_run));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(s[2 * pr + 1], c, -m_run));
+      const uint32_t wd = pack_bf16x2(p0, p1);
+      w[pr >> 2][pr & 3] = wd;
+      ls = (ls + __uint_as_float(wd << 16)) + __uint_as_float(wd & 0xFFFF0000u);
+    };
+    __builtin_amdgcn_sched_barrier(0);
+    if (t > 0) {
+      bf16x8 pf[kWaves];
+#pragma unroll
+      for (int g = 0; g < kGroups; ++g) {
+        pv_group(t - 1, g, pf);
+        word(g);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int pr = 0; pr < 8; ++pr) word(pr);
+    }
+    asm volatile("" : "+v"(ls));
     const bool over = __builtin_amdgcn_ballot_w64(ls > kCheck) != 0;
     if (over) m_run = fmaxf(m_run, col_max(s, c) + kOff);
     l_run += ls;
 #pragma unroll
     for (int u = 0; u < 2; ++u)
-      *reinterpret_cast<u32x4*>(smem + kOffP + ((wave * 2 + u) * 64 + lane) * 16) =
+      *reinterpret_cast<u32x4*>(smem + kOffP + (unsigned(t) & 1u) * kPB + ((wave * 2 + u) * 64 + lane) * 16) =
           u32x4{w[u][0], w[u][1], w[u][2], w[u][3]};
-    if (lane == 0) *reinterpret_cast<int*>(smem + kOffF + wave * 4) = over ? 1 : 0;
-    barrier_wait<63>();  // probabilities and flags visible; the next tile's loads stay in flight
+    if (lane == 0) *reinterpret_cast<int*>(smem + kOffF + (unsigned(t) & 1u) * 16 + wave * 4) = over ? 1 : 0;
+    barrier_wait<0>();  // tile t's probabilities and flags visible; K tile t+1 and V tile t have landed
 
     // ---- restart (rare): some query's reference was raised; every wave
     // starts over from the first tile (the raised references carry over)
     {
-      const i32x4 fl = *reinterpret_cast<const i32x4*>(smem + kOffF);
+      const i32x4 fl = *reinterpret_cast<const i32x4*>(smem + kOffF + (unsigned(t) & 1u) * 16);
       if (__builtin_amdgcn_readfirstlane(fl[0] | fl[1] | fl[2] | fl[3]) != 0) {
 #pragma unroll
         for (int b = 0; b < kWaves; ++b)
@@ -334,44 +371,20 @@ __global__ __launch_bounds__(kThreads) void attn_d512_kernel(const uint16_t* __r
           for (int ct = 0; ct < kCT; ++ct)
             acc[b][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zb, zb, f32x16{}, 0, 0, 0);
         l_run = 0.f;
-        barrier_wait<0>();  // the next tile's loads have landed and every wave has read the flags
-        load_tile(kh, vh, min(skv, kBN), rowbytes, kslot(0), vslot(0), wave, lane16);
+        load_rows(kh, 0, kslot(0), kKS);
+        barrier_wait<0>();  // K tile 0 has landed and every wave has read the flags
         t = -1;
         continue;
       }
     }
-
-    // ---- O^T[cols of this wave][queries of block b] += V^T P^T over the tile
-    __builtin_amdgcn_sched_barrier(0);
-    {
-      auto pread = [&](int b, int u) {
-        return *reinterpret_cast<const bf16x8*>(smem + kOffP + ((b * 2 + u) * 64 + lane) * 16);
-      };
-      // V^T operand of MFMA u, column tile ct: channels [32 ct, 32 ct + 32) of
-      // this wave x the 16 keys of u, in the key order of the probability words.
-      auto vread = [&](int u, int ct) {
-        const char* p0 = vb + u * 16 * kVS + ct * 64;
-        const i16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
-        const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 8 * kVS));
-        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
-      };
+  }
+  // ---- P*V of the last tile
+  {
+    bf16x8 pf[kWaves];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        bf16x8 pf[kWaves];
-#pragma unroll
-        for (int b = 0; b < kWaves; ++b) pf[b] = pread(b, u);
-        bf16x8 vf = vread(u, 0);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int ct = 0; ct < kCT; ++ct) {
-          const bf16x8 vc = vf;
-          if (ct + 1 < kCT) vf = vread(u, ct + 1);
-#pragma unroll
-          for (int b = 0; b < kWaves; ++b)
-            acc[b][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vc, pf[b], acc[b][ct], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
+    for (int g = 0; g < kGroups; ++g) {
+      pv_group(nT - 1, g, pf);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
