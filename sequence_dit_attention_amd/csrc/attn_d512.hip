@@ -254,6 +254,7 @@ __global__ __launch_bounds__(kThreads) void attn_d512_kernel(const uint16_t* __r
     for (int ct = 0; ct < kCT; ++ct) acc[b][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zb, zb, f32x16{}, 0, 0, 0);
   float m_run = -INFINITY;  // this wave's query block: reference (log2 units), the same in both halves
   float l_run = 0.f;        // the lane's partial row sum
+  barrier_wait<0>();  // K tile 0 has landed (each wave loaded 8 of its rows)
 
   const char* lds = reinterpret_cast<const char*>(smem);
   // Per-lane operand bases: K row `col`, chunk hf (+32 bytes per k-step);
