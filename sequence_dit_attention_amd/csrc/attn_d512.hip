@@ -22,12 +22,19 @@
 // and 128 queries: 256 MFMAs of 32x32x16 against 160 KiB of LDS operand reads
 // and 64 KiB of tile writes.
 //
-// Software pipeline, one barrier per tile: a wave computes the scores of tile
-// t, then makes their probabilities while its P*V MFMAs of tile t-1 run (the
-// probabilities of tile t-1 are in LDS since the previous barrier), writes
-// them to the other of two P buffers, and meets the other waves.  K tile t+1
-// loads during tile t into the slot K tile t-1 used; V tile t loads during
-// tile t into the slot of V tile t-2, which the P*V of tile t-1 does not read.
+// Software pipeline, one barrier per tile.  Step t turns the scores of tile
+// t (formed in step t-1) into probabilities while the matrix pipe runs two
+// streams: the scores of tile t+1 and P*V of tile t-1 (whose probabilities
+// are in LDS since the previous barrier).  The step is written out by hand,
+// one score MFMA and one P*V MFMA at a time, each followed by the few loads,
+// LDS reads and softmax instructions that can issue while it runs (in-order
+// issue would otherwise hold them behind a burst of MFMAs, or the MFMAs behind
+// a burst of tile loads).  The probabilities of tile t go to the second of two
+// P buffers; then the one barrier.  K tile t+2 loads during step t into the
+// slot of K tile t and V tile t into that of V tile t-2.  The first step's
+// P*V of "tile -1" multiplies zero probabilities with finite values and the
+// last step's scores of "tile nT" read a slot nobody writes then: both add
+// nothing and keep the step free of branches (1.6% more MFMAs for 64 tiles).
 // Row sums add the two bf16 halves of each probability word as float32 (the
 // weights P*V uses, exactly; v_dot2 would wait for the wave's MFMAs).
 //
@@ -231,6 +238,13 @@ __global__ __launch_bounds__(kThreads) void attn_d512_kernel(const uint16_t* __r
       lds_load(rs, slot + r * stride, uint32_t(r < valid ? r : valid - 1) * rowbytes, lane16);
     }
   };
+  // Row jj of this wave's part of K tile j / V tile j.
+  auto load_row = [&](const char* base, int j, uint32_t slot, int stride, int jj) __attribute__((always_inline)) {
+    const i32x4 rs = rsrc(base + int64_t(j) * tb);
+    const int valid = min(skv - j * kBN, kBN);
+    const int r = wave * kRowsW + jj;
+    lds_load(rs, slot + r * stride, uint32_t(r < valid ? r : valid - 1) * rowbytes, lane16);
+  };
   load_rows(kh, 0, kslot(0), kKS);
 
   // Q fragments of this wave's query block (B operand of S^T = K Q^T): lane
@@ -254,7 +268,6 @@ __global__ __launch_bounds__(kThreads) void attn_d512_kernel(const uint16_t* __r
     for (int ct = 0; ct < kCT; ++ct) acc[b][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zb, zb, f32x16{}, 0, 0, 0);
   float m_run = -INFINITY;  // this wave's query block: reference (log2 units), the same in both halves
   float l_run = 0.f;        // the lane's partial row sum
-  barrier_wait<0>();  // K tile 0 has landed (each wave loaded 8 of its rows)
 
   const char* lds = reinterpret_cast<const char*>(smem);
   // Per-lane operand bases: K row `col`, chunk hf (+32 bytes per k-step);
@@ -289,34 +302,57 @@ __global__ __launch_bounds__(kThreads) void attn_d512_kernel(const uint16_t* __r
   };
   constexpr int kGroups = 2 * kCT;  // MFMA groups of a tile's P*V
 
-  // Tile t: the scores of this wave's block; then, under the P*V MFMAs of
-  // tile t-1, their softmax; the probabilities and the raise flag to LDS; one
-  // barrier.  K tile t+1 and V tile t load during the tile (K tile t+1 into
-  // the slot of K tile t-1, read before the last barrier; V tile t into that
-  // of V tile t-2, read during tile t-1).
-  for (int t = 0; t < nT; ++t) {
-    if (t + 1 < nT) load_rows(kh, t + 1, kslot(t + 1), kKS);
-    load_rows(vh, t, vslot(t), kVS);
-    const char* kb = lds + (kslot(t) - sbase) + koff;
-
-    // ---- scores of this wave's query block over the tile's 32 keys; the K
-    // operands are read kKRA MFMAs ahead, each read-MFMA pair fenced in order
-    f32x16 s;
-    {
-      auto kread = [&](int cc) { return *reinterpret_cast<const bf16x8*>(kb + 32 * cc); };
-      bf16x8 kf[kKRA];
+  // Scores S^T of this wave's block over the 32 keys of tile j, in kGroups
+  // slices of 4 MFMAs; the K operands are read kKRA MFMAs ahead.
+  auto kbase = [&](int j) { return lds + (kslot(j) - sbase) + koff; };
+  auto kread = [&](const char* kb, int cc) { return *reinterpret_cast<const bf16x8*>(kb + 32 * cc); };
+  auto s_slice = [&](f32x16& d, const char* kb, bf16x8 (&kf)[kKRA], int g) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < kKRA; ++i) kf[i] = kread(i);
+    for (int i = 0; i < 4; ++i) {
+      const int cc = 4 * g + i;
+      const bf16x8 a = kf[cc % kKRA];
+      if (cc + kKRA < kDC) kf[cc % kKRA] = kread(kb, cc + kKRA);
+      if (cc == 0) d = mfma_s_first(a, qf[0]);
+      else if (cc + 1 < kDC) mfma_s(d, a, qf[cc]);
+      else mfma_s_last(d, a, qf[cc]);
+    }
+  };
+  auto scores_alone = [&](f32x16& d, int j) __attribute__((always_inline)) {
+    const char* kb = kbase(j);
+    bf16x8 kf[kKRA];
+#pragma unroll
+    for (int i = 0; i < kKRA; ++i) kf[i] = kread(kb, i);
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) {
+      s_slice(d, kb, kf, g);
       __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // The first step's P*V of "tile -1" multiplies zero probabilities (this
+  // wave's block in the second P buffer) with finite values (V tile 0 loaded
+  // into the second V slot): it adds exact zeros.
+  auto zero_p1 = [&]() __attribute__((always_inline)) {
 #pragma unroll
-      for (int cc = 0; cc < kDC; ++cc) {
-        const bf16x8 a = kf[cc % kKRA];
-        if (cc + kKRA < kDC) kf[cc % kKRA] = kread(cc + kKRA);
-        if (cc == 0) s = mfma_s_first(a, qf[0]);
-        else if (cc + 1 < kDC) mfma_s(s, a, qf[cc]);
-        else mfma_s_last(s, a, qf[cc]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    for (int u = 0; u < 2; ++u)
+      *reinterpret_cast<u32x4*>(smem + kOffP + kPB + ((wave * 2 + u) * 64 + lane) * 16) = u32x4{0u, 0u, 0u, 0u};
+  };
+  // Prologue: K tiles 0 and 1, the scores of tile 0.
+  if (nT > 1) load_rows(kh, 1, kslot(1), kKS);
+  load_rows(vh, 0, vslot(1), kVS);
+  zero_p1();
+  barrier_wait<0>();
+  f32x16 s;
+  scores_alone(s, 0);
+
+  // Step t: the softmax of tile t (its scores are in s) under two MFMA
+  // streams, the scores of tile t+1 and P*V of tile t-1, a slice of each per
+  // pair of probability words; then the probabilities of tile t and the raise
+  // flag to LDS and one barrier.  K tile t+2 loads into the slot of K tile t
+  // (read during step t-1) and V tile t into that of V tile t-2 (read during
+  // step t-1); both land before the barrier.
+  for (int t = 0; t < nT; ++t) {
+    {
       const int key_last = skv - t * kBN;  // keys at or past this index are masked
       if (key_last < kBN) {
 #pragma unroll
@@ -324,42 +360,79 @@ __global__ __launch_bounds__(kThreads) void attn_d512_kernel(const uint16_t* __r
           if (8 * (r >> 2) + 4 * hf + (r & 3) >= key_last) s[r] = -INFINITY;
       }
     }
-
-    // ---- softmax of the block (float32 row sums: v_dot2 would wait for the
-    // MFMA pipe) under the P*V of tile t-1
     if (t == 0) m_run = fmaxf(m_run, col_max(s, c) + kOff);  // every column has a key in the first tile
     uint32_t w[2][4];
-    float ls = 0.f;
-    auto word = [&](int pr) __attribute__((always_inline)) {
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[2 * pr], c, -m_run));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(s[2 * pr + 1], c, -m_run));
-      const uint32_t wd = pack_bf16x2(p0, p1);
-      w[pr >> 2][pr & 3] = wd;
-      ls = (ls + __uint_as_float(wd << 16)) + __uint_as_float(wd & 0xFFFF0000u);
-    };
+    float ls = 0.f, mx = -INFINITY;
+    f32x16 sn;
     __builtin_amdgcn_sched_barrier(0);
-    if (t > 0) {
-      bf16x8 pf[kWaves];
+    {
+      const char* kb = kbase(t + 1);
+      const int jk = min(t + 2, nT - 1);  // past the last tile: the last again, into a slot nobody reads
+      bf16x8 kf[kKRA], pf[kWaves];
+#pragma unroll
+      for (int i = 0; i < kKRA; ++i) kf[i] = kread(kb, i);
+#pragma unroll
+      for (int b = 0; b < kWaves; ++b) pf[b] = pread(t - 1, b, 0);
+      bf16x8 vcur = vread(t - 1, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int g = 0; g < kGroups; ++g) {
-        pv_group(t - 1, g, pf);
-        word(g);
+        const int ct = g % kCT;
+        const int gn = g + 1, un = gn / kCT, ctn = gn % kCT;
+        bf16x8 vnext = vcur;
+        auto smf = [&](int i) __attribute__((always_inline)) {
+          const int cc = 4 * g + i;
+          const bf16x8 a = kf[cc % kKRA];
+          if (cc + kKRA < kDC) kf[cc % kKRA] = kread(kb, cc + kKRA);
+          if (cc == 0) sn = mfma_s_first(a, qf[0]);
+          else if (cc + 1 < kDC) mfma_s(sn, a, qf[cc]);
+          else mfma_s_last(sn, a, qf[cc]);
+        };
+        auto pvf = [&](int b) __attribute__((always_inline)) {
+          acc[b][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vcur, pf[b], acc[b][ct], 0, 0, 0);
+          if (gn < kGroups && ctn == 0) pf[b] = pread(t - 1, b, un);
+        };
+        const int pr = g;
+        float p0, p1;
+        uint32_t wd;
+        smf(0);
+        load_row(vh, t, vslot(t), kVS, g);
         __builtin_amdgcn_sched_barrier(0);
+        pvf(0);
+        mx = __builtin_fmaxf(mx, __builtin_fmaxf(s[2 * pr], s[2 * pr + 1]));
+        p0 = __builtin_amdgcn_exp2f(fmaf(s[2 * pr], c, -m_run));
+        __builtin_amdgcn_sched_barrier(0);
+        smf(1);
+        load_row(kh, jk, kslot(t + 2), kKS, g);
+        __builtin_amdgcn_sched_barrier(0);
+        pvf(1);
+        p1 = __builtin_amdgcn_exp2f(fmaf(s[2 * pr + 1], c, -m_run));
+        __builtin_amdgcn_sched_barrier(0);
+        smf(2);
+        if (gn < kGroups) vnext = vread(t - 1, un, ctn);
+        __builtin_amdgcn_sched_barrier(0);
+        pvf(2);
+        wd = pack_bf16x2(p0, p1);
+        w[pr >> 2][pr & 3] = wd;
+        __builtin_amdgcn_sched_barrier(0);
+        smf(3);
+        __builtin_amdgcn_sched_barrier(0);
+        pvf(3);
+        ls = (ls + __uint_as_float(wd << 16)) + __uint_as_float(wd & 0xFFFF0000u);
+        __builtin_amdgcn_sched_barrier(0);
+        vcur = vnext;
       }
-    } else {
-#pragma unroll
-      for (int pr = 0; pr < 8; ++pr) word(pr);
     }
     asm volatile("" : "+v"(ls));
     const bool over = __builtin_amdgcn_ballot_w64(ls > kCheck) != 0;
-    if (over) m_run = fmaxf(m_run, col_max(s, c) + kOff);
+    if (over) m_run = fmaxf(m_run, halves_max(mx) * c + kOff);
     l_run += ls;
 #pragma unroll
     for (int u = 0; u < 2; ++u)
       *reinterpret_cast<u32x4*>(smem + kOffP + (unsigned(t) & 1u) * kPB + ((wave * 2 + u) * 64 + lane) * 16) =
           u32x4{w[u][0], w[u][1], w[u][2], w[u][3]};
     if (lane == 0) *reinterpret_cast<int*>(smem + kOffF + (unsigned(t) & 1u) * 16 + wave * 4) = over ? 1 : 0;
-    barrier_wait<0>();  // tile t's probabilities and flags visible; K tile t+1 and V tile t have landed
+    barrier_wait<0>();  // tile t's probabilities and flags visible; K tile t+2 and V tile t have landed
 
     // ---- restart (rare): some query's reference was raised; every wave
     // starts over from the first tile (the raised references carry over)
@@ -372,12 +445,16 @@ __global__ __launch_bounds__(kThreads) void attn_d512_kernel(const uint16_t* __r
           for (int ct = 0; ct < kCT; ++ct)
             acc[b][ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zb, zb, f32x16{}, 0, 0, 0);
         l_run = 0.f;
+        zero_p1();
         load_rows(kh, 0, kslot(0), kKS);
-        barrier_wait<0>();  // K tile 0 has landed and every wave has read the flags
+        if (nT > 1) load_rows(kh, 1, kslot(1), kKS);
+        barrier_wait<0>();  // K tiles 0 and 1 have landed and every wave has read the flags
+        scores_alone(s, 0);
         t = -1;
         continue;
       }
     }
+    s = sn;
   }
   // ---- P*V of the last tile
   {
