@@ -120,3 +120,27 @@ def test_d512_restarts_on_large_score_jumps(nsplit):
     torch.cuda.synchronize()
     assert np.isfinite(to_f64(o)).all()
     _check(o, lse, qb, kb, vb)
+
+
+@pytest.mark.parametrize("skv,nsplit,pos", [(96, 1, [0, 1, 40, 70]), (128, 2, [0, 1, 40, 41, 64, 65, 100, 101]),
+                                            (64, 1, [0, 1, 33, 34]), (33, 1, [0, 1, 32])],
+                         ids=["3tiles", "2x2tiles", "2tiles", "ragged2"])
+def test_d512_restart_in_the_last_step_of_short_ranges(skv, nsplit, pos):
+    """Head size 512 on ranges of two or three 32-key tiles, with the spike that forces a
+    restart in the range's last tile: the restart comes after the last step, whose
+    scores of the tile past the range are discarded, and the K tile of that step's
+    load is the last one again.  The first spike of each axis sits in the first tile
+    (it sets the reference); the later ones climb ~120 each.  In the 2 x 2 case each
+    range restarts in its own last step; the ragged case has one key in its last
+    tile, the spike."""
+    sq, d = 160, 512
+    qb, kb, vb = _restart_inputs(sq, skv, d, 21 + skv, pos)
+    q, k, v = (to_dev(a, "bf16") for a in (qb, kb, vb))
+    lse = torch.empty(1, sq, dtype=torch.float32, device="cuda")
+    if nsplit == 1:
+        o = sp.shard_attn_fwd(q, k, v, lse=lse)
+    else:
+        o = sp.shard_attn_fwd_split(q, k, v, nsplit=nsplit, lse=lse)
+    torch.cuda.synchronize()
+    assert np.isfinite(to_f64(o)).all()
+    _check(o, lse, qb, kb, vb)
