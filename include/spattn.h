@@ -356,9 +356,11 @@ int shard_attn_fwd_split(int32_t dtype, const void* q, const void* k, const void
 
 /*
  * sp_attn_split_workspace -- bytes of workspace shard_attn_fwd_split needs:
- * nsplit*sq*H*d float32 partial outputs (rounded up to 256 bytes) followed by
- * nsplit*H*sq float32 partial log-sum-exps.  Negative status on bad
- * arguments (SP_EINVAL) or overflow (SP_ERANGE).  Host-only.
+ * nsplit*rows*H*d float32 partial outputs (rounded up to 256 bytes) followed
+ * by nsplit*H*sq float32 partial log-sum-exps, where rows = sq, or at d = 512
+ * sq rounded up to a multiple of 128 (that kernel writes whole 128-query
+ * blocks).  Negative status on bad arguments (SP_EINVAL) or overflow
+ * (SP_ERANGE).  Host-only.
  */
 int64_t sp_attn_split_workspace(int64_t sq, int32_t H, int32_t d, int32_t nsplit);
 

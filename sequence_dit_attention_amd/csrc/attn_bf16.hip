@@ -948,6 +948,7 @@ int64_t attn_bf16_items(int64_t sq, int H, int d, int nsplit) {
 }
 
 int64_t attn_merge_items(int64_t sq, int H, int d) {
+  if (d == 512) return attn_d512_merge_items(sq, H);
   const __int128 n = (__int128(sq) * H * (d / 4) + 255) / 256 * 256;
   return n > INT64_MAX ? INT64_MAX : int64_t(n);
 }
@@ -1012,8 +1013,12 @@ hipError_t launch_attn_bf16_split(const void* q, const void* k, const void* v, v
   // fit enqueues nothing.
   if (attn_bf16_items(sq, H, d, nsplit) > kMaxItems || attn_merge_items(sq, H, d) > kMaxItems)
     return hipErrorInvalidConfiguration;
-  hipError_t e = d == 512 ? launch_attn_d512(q, k, v, o, lpart, sq, skv, H, c, nsplit, opart, stream)
-                          : launch_attn_d128(q, k, v, o, lpart, sq, skv, H, c, nsplit, opart, stream);
+  if (d == 512) {
+    hipError_t e = launch_attn_d512(q, k, v, o, lpart, sq, skv, H, c, nsplit, opart, stream);
+    if (e != hipSuccess) return e;
+    return launch_merge_d512(opart, lpart, o, lse, nsplit, sq, H, stream);
+  }
+  hipError_t e = launch_attn_d128(q, k, v, o, lpart, sq, skv, H, c, nsplit, opart, stream);
   if (e != hipSuccess) return e;
   return launch_merge(opart, lpart, o, lse, nsplit, sq, H, d, stream);
 }

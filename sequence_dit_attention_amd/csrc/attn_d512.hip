@@ -181,7 +181,8 @@ __device__ inline float col_max(const f32x16& s, float c) {
 
 // SPLIT: the keys are cut into nsplit ranges of whole tiles; work-group
 // (range, query tile, head) writes its float32 O normalised over its own keys
-// (opart [nsplit, sq, H, 512]) and that range's LSE (lse [nsplit, H, sq]).
+// as one 128 x 512 block (opart: [nsplit, H, query tiles] blocks, the layout
+// of the epilogue) and that range's LSE (lse [nsplit, H, sq]).
 // Ranges vary fastest over the work-groups, so with 8 ranges the work-groups
 // of one range share an XCD (and its L2) when blocks are dealt round-robin.
 template <bool SPLIT>
@@ -478,23 +479,38 @@ __global__ __launch_bounds__(kThreads) void attn_d512_kernel(const uint16_t* __r
     }
   }
   barrier_wait<0>();
+  if constexpr (SPLIT) {
+    // Partial block of this work-group, in the order of the accumulators:
+    // [wave][query block][column tile][row group][lane] x 16 bytes, so every
+    // store is one contiguous KiB.  Rows past sq are written too (finite: they
+    // repeat row sq-1) and the merge skips them.
+    float* const blk = opart + ((int64_t(sp) * H + h) * nqt + qt) * int64_t(kBM * kD);
 #pragma unroll
-  for (int b = 0; b < kWaves; ++b) {
-    const int row = qt * kBM + b * 32 + col;
-    const float inv = 1.f / *reinterpret_cast<const float*>(smem + kOffL + (b * 32 + col) * 4);
-    if (row >= sq) continue;
+    for (int b = 0; b < kWaves; ++b) {
+      const float inv = 1.f / *reinterpret_cast<const float*>(smem + kOffL + (b * 32 + col) * 4);
 #pragma unroll
-    for (int ct = 0; ct < kCT; ++ct) {
-      const int cb = wave * kColsW + ct * 32;
+      for (int ct = 0; ct < kCT; ++ct) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = cb + 8 * g + 4 * hf;
-        const f32x16& a = acc[b][ct];
-        if (SPLIT) {
-          float* dst = opart + (int64_t(sp) * sq + row) * rowstride + int64_t(h) * kD + d0;
-          *reinterpret_cast<f32x4*>(dst) =
+        for (int g = 0; g < 4; ++g) {
+          const f32x16& a = acc[b][ct];
+          *reinterpret_cast<f32x4*>(blk + ((((wave * kWaves + b) * kCT + ct) * 4 + g) * 64 + lane) * 4) =
               f32x4{a[4 * g] * inv, a[4 * g + 1] * inv, a[4 * g + 2] * inv, a[4 * g + 3] * inv};
-        } else {
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int b = 0; b < kWaves; ++b) {
+      const int row = qt * kBM + b * 32 + col;
+      const float inv = 1.f / *reinterpret_cast<const float*>(smem + kOffL + (b * 32 + col) * 4);
+      if (row >= sq) continue;
+#pragma unroll
+      for (int ct = 0; ct < kCT; ++ct) {
+        const int cb = wave * kColsW + ct * 32;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = cb + 8 * g + 4 * hf;
+          const f32x16& a = acc[b][ct];
           uint16_t* dst = o + int64_t(row) * rowstride + int64_t(h) * kD + d0;
           *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(a[4 * g] * inv, a[4 * g + 1] * inv),
                                                  pack_bf16x2(a[4 * g + 2] * inv, a[4 * g + 3] * inv)};
@@ -504,11 +520,62 @@ __global__ __launch_bounds__(kThreads) void attn_d512_kernel(const uint16_t* __r
   }
 }
 
+// Merge of the key ranges of a split launch (the partial blocks above): with
+// m = max_s lse_s and w_s = exp(lse_s - m), O = sum_s w_s O_s / sum_s w_s
+// (rounded once to bf16) and LSE = m + log(sum_s w_s), in float32.  One
+// thread per 16-byte piece of a block, the same place in every range's block;
+// the weights and the order of the sum are those of the row-major merge of the
+// other head sizes.  HBM-bound: reads the partials once.
+__global__ __launch_bounds__(256) void merge_d512_kernel(const float* __restrict__ opart,
+                                                         const float* __restrict__ lpart, uint16_t* __restrict__ o,
+                                                         float* __restrict__ lse, int nsplit, int sq, int H,
+                                                         int nqt) {
+  constexpr int kPieces = kBM * kD / 4;  // 16-byte pieces of one block
+  const int64_t gid = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t blkid = gid / kPieces;  // h * nqt + qt
+  if (blkid >= int64_t(H) * nqt) return;
+  const int c = int(gid - blkid * kPieces);
+  const int h = int(blkid / nqt), qt = int(blkid - int64_t(h) * nqt);
+  const int ln = c & 63, g = (c >> 6) & 3, ct = (c >> 8) & (kCT - 1), b = (c >> 10) & (kWaves - 1), w = c >> 12;
+  const int row = qt * kBM + b * 32 + (ln & 31);
+  if (row >= sq) return;
+  const int ch = w * kColsW + ct * 32 + 8 * g + 4 * (ln >> 5);
+  float m = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) m = fmaxf(m, lpart[(int64_t(s) * H + h) * sq + row]);
+  float ws = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < nsplit; ++s) {
+    const float wgt = expf(lpart[(int64_t(s) * H + h) * sq + row] - m);
+    const f32x4 x = *reinterpret_cast<const f32x4*>(opart + ((int64_t(s) * H + h) * nqt + qt) * int64_t(kBM * kD) +
+                                                    int64_t(c) * 4);
+    ws += wgt;
+    acc += wgt * x;
+  }
+  const float inv = 1.f / ws;
+  *reinterpret_cast<u32x2*>(o + (int64_t(row) * H + h) * kD + ch) =
+      u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+  if (lse && ch == 0) lse[int64_t(h) * sq + row] = m + logf(ws);
+}
+
 }  // namespace
 
 int64_t attn_d512_items(int64_t sq, int H, int nsplit) {
   const __int128 n = __int128((sq + kBM - 1) / kBM) * H * nsplit * kThreads;
   return n > INT64_MAX ? INT64_MAX : int64_t(n);
+}
+
+int64_t attn_d512_merge_items(int64_t sq, int H) {
+  const __int128 n = __int128((sq + kBM - 1) / kBM) * H * (kBM * kD / 4);
+  return n > INT64_MAX ? INT64_MAX : int64_t(n);
+}
+
+hipError_t launch_merge_d512(const float* opart, const float* lpart, void* o, float* lse, int nsplit, int64_t sq,
+                             int H, hipStream_t stream) {
+  const int64_t nqt = (sq + kBM - 1) / kBM;
+  const int64_t blocks = nqt * H * (kBM * kD / 4) / 256;  // the host has checked the items against kMaxItems
+  hipLaunchKernelGGL(merge_d512_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, opart, lpart,
+                     static_cast<uint16_t*>(o), lse, nsplit, int(sq), H, int(nqt));
+  return hipGetLastError();
 }
 
 hipError_t launch_attn_d512(const void* q, const void* k, const void* v, void* o, float* lse, int64_t sq,

@@ -508,7 +508,9 @@ int shard_attn_fwd(int32_t dtype, const void* q, const void* k, const void* v, v
 int64_t sp_attn_split_workspace(int64_t sq, int32_t H, int32_t d, int32_t nsplit) {
   if (sq < 0 || H < 1 || d < 1 || nsplit < 1) return fail(SP_EINVAL, "sp_attn_split_workspace: bad arguments");
   int64_t on, ob, ln, lbytes;
-  if (!mul_ok(sq, int64_t(H) * d, &on) || !mul_ok(on, int64_t(nsplit) * 4, &ob) || !mul_ok(sq, int64_t(H), &ln) ||
+  if (sq > (int64_t(1) << 60)) return fail(SP_ERANGE, "sp_attn_split_workspace: size overflows int64");
+  if (!mul_ok(spattn::split_rows(sq, d), int64_t(H) * d, &on) || !mul_ok(on, int64_t(nsplit) * 4, &ob) ||
+      !mul_ok(sq, int64_t(H), &ln) ||
       !mul_ok(ln, int64_t(nsplit) * 4, &lbytes) || ob > (int64_t(1) << 60) || lbytes > (int64_t(1) << 60))
     return fail(SP_ERANGE, "sp_attn_split_workspace: size overflows int64");
   ok();
@@ -550,7 +552,7 @@ int check_split(const char* fn, int32_t dtype, const void* q, const void* k, con
 // (at the next 256-byte boundary).
 int launch_split_in(const char* fn, const void* q, const void* k, const void* v, void* o, float* lse, int64_t sq,
                     int64_t skv, int32_t H, int32_t d, float scale, int32_t nsplit, void* workspace, void* stream) {
-  const int64_t ob = sq * H * d * int64_t(nsplit) * 4;
+  const int64_t ob = spattn::split_rows(sq, d) * H * d * int64_t(nsplit) * 4;  // checked by the size query
   float* opart = static_cast<float*>(workspace);
   float* lpart = reinterpret_cast<float*>(static_cast<char*>(workspace) + ((ob + 255) / 256) * 256);
   (void)hipGetLastError();

@@ -60,8 +60,8 @@ struct KvShards {
 // Attention against sharded K/V (same results as the gathered call on the
 // concatenation of the shards).
 // Split-key attention: nsplit launches' worth of key ranges in one launch
-// writing float32 partials (opart [nsplit, sq, H, d], lpart [nsplit, H, sq]),
-// then a merge into o (bf16) and lse (may be null).
+// writing float32 partials (opart: split_rows(sq, d) x H x d floats per range,
+// lpart [nsplit, H, sq]), then a merge into o (bf16) and lse (may be null).
 hipError_t launch_attn_bf16_split(const void* q, const void* k, const void* v, void* o, float* lse, int64_t sq,
                                   int64_t skv, int H, int d, float scale, int nsplit, float* opart, float* lpart,
                                   hipStream_t stream);
@@ -73,15 +73,24 @@ hipError_t launch_attn_f32_gv(const float* q, const KvShards& kv, float* o, floa
 // Head size 512 (bf16, its own kernel: every score formed once).  c is the
 // softmax scale times log2(e).  opart == nullptr: writes o and lse (may be
 // null); otherwise the keys are cut into nsplit ranges and the call writes
-// float32 partials opart [nsplit, sq, H, 512] and their LSE into lse
-// ([nsplit, H, sq]) for the merge of launch_attn_bf16_split.
+// float32 partials, one 128-query x 512 block per (range, head, query tile)
+// in the order of the kernel's accumulators, and their LSE into lse
+// ([nsplit, H, sq]); launch_merge_d512 combines them.
 hipError_t launch_attn_d512(const void* q, const void* k, const void* v, void* o, float* lse, int64_t sq,
                             int64_t skv, int H, float c, int nsplit, float* opart, hipStream_t stream);
+hipError_t launch_merge_d512(const float* opart, const float* lpart, void* o, float* lse, int nsplit, int64_t sq,
+                             int H, hipStream_t stream);
 int64_t attn_d512_items(int64_t sq, int H, int nsplit);
+int64_t attn_d512_merge_items(int64_t sq, int H);
+
+// Rows of float32 partials per (range, head) that a split launch writes: sq,
+// or for head size 512 sq rounded up to whole 128-query tiles.
+inline int64_t split_rows(int64_t sq, int d) { return d == 512 ? (sq + 127) / 128 * 128 : sq; }
 
 // Head size 128 (bf16, eight waves per work-group, two per SIMD).  c is the
 // softmax scale times log2(e).  opart == nullptr: writes o and lse (may be
-// null); otherwise key ranges and float32 partials as launch_attn_d512.
+// null); otherwise key ranges, float32 partials opart [nsplit, sq, H, 128] and
+// their LSE into lse ([nsplit, H, sq]).
 hipError_t launch_attn_d128(const void* q, const void* k, const void* v, void* o, float* lse, int64_t sq,
                             int64_t skv, int H, float c, int nsplit, float* opart, hipStream_t stream);
 hipError_t launch_attn_d128_gv(const void* q, const KvShards& kv, void* o, float* lse, int64_t sq, int H, float c,

@@ -231,6 +231,9 @@ def test_split_attention_validation():
     L = _lib.lib()
     ws = L.sp_attn_split_workspace
     assert ws(100, 2, 128, 3) == ((3 * 100 * 2 * 128 * 4 + 255) // 256) * 256 + 3 * 2 * 100 * 4
+    # head size 512 writes whole 128-query blocks of partials: rows rounded up to 128
+    assert ws(100, 2, 512, 3) == ((3 * 128 * 2 * 512 * 4 + 255) // 256) * 256 + 3 * 2 * 100 * 4
+    assert ws(4096, 1, 512, 8) == 8 * 4096 * 512 * 4 + 8 * 4096 * 4
     assert ws(-1, 2, 128, 3) == SP_EINVAL and ws(10, 2, 128, 0) == SP_EINVAL
     assert ws(2**40, 2**20, 512, 1024) == SP_ERANGE
     f = L.shard_attn_fwd_split
