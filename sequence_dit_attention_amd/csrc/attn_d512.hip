@@ -19,8 +19,8 @@
 // So every score is formed once, a lane holds 128 Q registers (VGPRs) and 256
 // accumulators (4 blocks x 4 column tiles x 16, all the AGPRs), and each K
 // operand read from LDS feeds one MFMA, each V^T operand four.  Per 32 keys
-// and 128 queries: 256 MFMAs of 32x32x16 against 160 KiB of LDS operand reads
-// and 64 KiB of tile writes.
+// and 128 queries: 256 MFMAs of 32x32x16 against 192 KiB of LDS operand reads
+// (K 128, P 32, V 32) and 64 KiB of tile writes.
 //
 // Software pipeline, one barrier per tile.  Step t turns the scores of tile
 // t (formed in step t-1) into probabilities while the matrix pipe runs two
