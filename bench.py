@@ -412,6 +412,16 @@ def main() -> int:
         torch.cuda.synchronize()
         vms = [sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.vae_steps)) / args.vae_steps
                for j in range(3)]
+        # The attention call alone (split attention + merge), back to back: one
+        # event pair around the calls, so the queue stays ahead of the GPU.
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b0.record()
+        for _ in range(args.vae_steps):
+            vs.attend()
+        b1.record()
+        torch.cuda.synchronize()
+        call_ms = b0.elapsed_time(b1) / args.vae_steps
+        call_tf = vs.attn_flops() / (call_ms * 1e-3) / 1e12
         # The same step replayed as a HIP graph (all five launches issued at once).
         graph_ms, replay_same = None, None
         if not args.vae_eager_only:
@@ -432,11 +442,13 @@ def main() -> int:
                "launch": "eager" if graph_ms is None else "hip_graph", "graph_equals_eager": replay_same,
                "eager_ms_per_step": sum(vms), "gather_kv_ms": vms[0], "attn_ms": vms[1], "place_out_ms": vms[2],
                "attn_tflops": va_tf, "attn_frac_mfma_peak": va_tf / PEAK_BF16_TFLOPS,
+               "attn_call_ms": call_ms, "attn_call_tflops": call_tf, "attn_call_frac_mfma_peak": call_tf / PEAK_BF16_TFLOPS,
                "copy_gbs": vs.copy_bytes() / ((vms[0] + vms[2]) * 1e-3) / 1e9}
         if replay_same is False:
             raise RuntimeError("VAE share: graph replay differs from the eager step")
         log(f"VAE block share: {vae['ms_per_step']:.3f} ms per step ({vae['launch']}), {sum(vms):.3f} ms eager "
-            f"(attention {vms[1]:.3f} ms, {va_tf:.0f} TFLOP/s)")
+            f"(attention {vms[1]:.3f} ms, {va_tf:.0f} TFLOP/s); attention call back to back {call_ms * 1e3:.1f} us "
+            f"({call_tf:.0f} TFLOP/s)")
 
     flops = share.attn_flops()
     attn_tflops = flops / (per["attn"] * 1e-3) / 1e12
