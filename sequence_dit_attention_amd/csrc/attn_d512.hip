@@ -250,7 +250,8 @@ __global__ __launch_bounds__(kThreads) void attn_d512_kernel(const uint16_t* __r
 
   // Q fragments of this wave's query block (B operand of S^T = K Q^T): lane
   // holds 8 channels of query `col` per k-step.  Rows past sq repeat row
-  // sq-1: their columns are computed and never written.
+  // sq-1: their columns are computed and never written to o (a split launch
+  // writes them into its partial block, which the merge skips).
   bf16x8 qf[kDC];
   {
     const int row = min(qt * kBM + wave * 32 + col, sq - 1);
@@ -342,7 +343,7 @@ __global__ __launch_bounds__(kThreads) void attn_d512_kernel(const uint16_t* __r
   if (nT > 1) load_rows(kh, 1, kslot(1), kKS);
   load_rows(vh, 0, vslot(1), kVS);
   zero_p1();
-  barrier_wait<0>();
+  barrier_wait<0>();  // K tiles 0 and 1 and V tile 0 have landed (each wave loads 8 rows of each); zeros visible
   f32x16 s;
   scores_alone(s, 0);
 
