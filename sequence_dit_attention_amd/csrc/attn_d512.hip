@@ -84,7 +84,7 @@ constexpr int kDC = kD / 16;                // k-steps of the score MFMA
 constexpr int kColsW = kD / kWaves;         // output columns per wave
 constexpr int kCT = kColsW / 32;            // 32-column O^T tiles per wave and query block
 constexpr int kRowsW = kBN / kWaves;        // tile rows each wave loads
-constexpr int kKRA = 4;                     // K operands read ahead of their MFMA
+constexpr int kKRA = 2;                     // K operands read ahead of their MFMA
 constexpr float kOff = 40.0f;               // reference above a query's first-tile maximum (log2 units)
 constexpr float kCheck = 18446744073709551616.0f;  // 2^64: a lane's sum of 16 probabilities above it restarts
 constexpr float kLn2 = 0.69314718055994531f;
