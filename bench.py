@@ -318,6 +318,18 @@ def main() -> int:
     log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (host wall {wall / args.steps * 1e3:.3f} ms); "
         + ", ".join(f"{s} {t:.3f} ms" for s, t in per.items()))
 
+    # The attention call alone, back to back (one event pair around the calls,
+    # the queue ahead of the GPU): on short workloads the per-stage events of a
+    # step also hold the host's launch gap before the call.
+    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    nb = max(args.steps, 3)
+    b0.record()
+    for _ in range(nb):
+        share.attend()
+    b1.record()
+    torch.cuda.synchronize()
+    attn_call_ms = b0.elapsed_time(b1) / nb
+
     # The gather-free variant of the same share (K/V read from the rank shards by
     # the attention kernel, no pack/unpack); reported beside the headline step.
     gf = None
@@ -475,6 +487,7 @@ def main() -> int:
                      "frac": attn_tflops / PEAK_BF16_TFLOPS, "traffic": traffic},
         "kernels": {
             "attn_ms": per["attn"], "attn_tflops": attn_tflops, "attn_frac_mfma_peak": attn_tflops / PEAK_BF16_TFLOPS,
+            "attn_call_ms": attn_call_ms, "attn_call_frac_mfma_peak": flops / (attn_call_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
             "pack_kv_ms": per["pack_kv"], "pack_kv_gbs": pack_gbs, "pack_frac_hbm_peak": pack_gbs / PEAK_HBM_GBS,
             "unpack_kv_ms": per["unpack_kv"], "unpack_kv_gbs": unpack_gbs,
             "rope_ms": per["rope"], "concat_out_ms": per["concat_out"],
