@@ -526,7 +526,8 @@ __global__ __launch_bounds__(kThreads) void attn_d512_kernel(const uint16_t* __r
 // (rounded once to bf16) and LSE = m + log(sum_s w_s), in float32.  One
 // thread per 16-byte piece of a block, the same place in every range's block;
 // the weights and the order of the sum are those of the row-major merge of the
-// other head sizes.  HBM-bound: reads the partials once.
+// other head sizes.  HBM-bound: reads the partials once, eight ranges' loads in
+// flight at a time (the LSEs for the maximum, then the partial pieces).
 __global__ __launch_bounds__(256) void merge_d512_kernel(const float* __restrict__ opart,
                                                          const float* __restrict__ lpart, uint16_t* __restrict__ o,
                                                          float* __restrict__ lse, int nsplit, int sq, int H,
@@ -542,16 +543,37 @@ __global__ __launch_bounds__(256) void merge_d512_kernel(const float* __restrict
   if (row >= sq) return;
   const int ch = w * kColsW + ct * 32 + 8 * g + 4 * (ln >> 5);
   float m = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) m = fmaxf(m, lpart[(int64_t(s) * H + h) * sq + row]);
+  {
+    int s = 0;
+    for (; s + 8 <= nsplit; s += 8) {
+      float l[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) l[i] = lpart[(int64_t(s + i) * H + h) * sq + row];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = fmaxf(m, l[i]);
+    }
+    for (; s < nsplit; ++s) m = fmaxf(m, lpart[(int64_t(s) * H + h) * sq + row]);
+  }
   float ws = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < nsplit; ++s) {
+  auto part = [&](int s) __attribute__((always_inline)) {
+    return *reinterpret_cast<const f32x4*>(opart + ((int64_t(s) * H + h) * nqt + qt) * int64_t(kBM * kD) +
+                                           int64_t(c) * 4);
+  };
+  auto add = [&](int s, const f32x4& x) __attribute__((always_inline)) {
     const float wgt = expf(lpart[(int64_t(s) * H + h) * sq + row] - m);
-    const f32x4 x = *reinterpret_cast<const f32x4*>(opart + ((int64_t(s) * H + h) * nqt + qt) * int64_t(kBM * kD) +
-                                                    int64_t(c) * 4);
     ws += wgt;
     acc += wgt * x;
+  };
+  int s = 0;
+  for (; s + 8 <= nsplit; s += 8) {
+    f32x4 x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = part(s + i);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) add(s + i, x[i]);
   }
+  for (; s < nsplit; ++s) add(s, part(s));
   const float inv = 1.f / ws;
   *reinterpret_cast<u32x2*>(o + (int64_t(row) * H + h) * kD + ch) =
       u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
