@@ -897,15 +897,41 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ op
   const int c4 = int(g - rh * per);
   const int64_t row = rh / H;
   const int h = int(rh - row * H);
+  // Eight ranges' loads in flight at a time (the LSEs for the maximum, then
+  // the partial pieces); the sum keeps the order of the ranges.
+  auto lse_of = [&](int s) { return lpart[(int64_t(s) * H + h) * sq + row]; };
+  auto part = [&](int s) {
+    return *reinterpret_cast<const f32x4*>(opart + (int64_t(s) * sq * H + rh) * D + 4 * c4);
+  };
   float m = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) m = fmaxf(m, lpart[(int64_t(s) * H + h) * sq + row]);
+  {
+    int s = 0;
+    for (; s + 8 <= nsplit; s += 8) {
+      float l[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) l[i] = lse_of(s + i);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = fmaxf(m, l[i]);
+    }
+    for (; s < nsplit; ++s) m = fmaxf(m, lse_of(s));
+  }
   float ws = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < nsplit; ++s) {
-    const float w = expf(lpart[(int64_t(s) * H + h) * sq + row] - m);
-    const f32x4 x = *reinterpret_cast<const f32x4*>(opart + (int64_t(s) * sq * H + rh) * D + 4 * c4);
+  auto add = [&](int s, const f32x4& x) __attribute__((always_inline)) {
+    const float w = expf(lse_of(s) - m);
     ws += w;
     acc += w * x;
+  };
+  {
+    int s = 0;
+    for (; s + 8 <= nsplit; s += 8) {
+      f32x4 x[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = part(s + i);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) add(s + i, x[i]);
+    }
+    for (; s < nsplit; ++s) add(s, part(s));
   }
   const float inv = 1.f / ws;
   u32x2 w2;
